@@ -1,0 +1,399 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself --
+values the pages print, library routines (NumPy's stable sort and bincount, torch's e4m3
+cast, SciPy's softmax/expit, torch's dense SwiGLU), closed forms, error bounds and
+invariants.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from mixture_experts_layer_sigmoid_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FLT_MAX = np.float32(np.finfo(np.float32).max)
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32_of_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.float().numpy()
+
+
+# ----------------------------------------------------------------------------- e4m3 codec
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([oracle.e4m3_decode(c) for c in range(256)], np.float32)
+    nan = np.isnan(ref)
+    assert set(np.nonzero(nan)[0]) == {0x7F, 0xFF}
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_max_finite_is_448():
+    g = golden("e4m3_saturation.json")
+    assert oracle.e4m3_decode(0x7E) == g["max_finite"] == 448.0
+    assert oracle.e4m3_encode(1e6) == 0x7E and oracle.e4m3_encode(-1e6) == 0xFE
+    assert oracle.e4m3_encode(448.0) == 0x7E
+
+
+def _encode_torch(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_matches_torch_on_midpoints_and_neighbours():
+    """Every representable value, every midpoint between neighbours, and the fp32 values one
+    ulp either side of each: round-to-nearest-even agrees with torch's cast."""
+    vals = np.array([oracle.e4m3_decode(c) for c in range(0x7F)], np.float64)  # 0 .. 448
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids]).astype(np.float32)
+    pts = np.concatenate([pts, np.nextafter(pts, np.float32(np.inf)), np.nextafter(pts, np.float32(0))])
+    pts = pts[(pts >= 0) & (pts <= 448)]
+    pts = np.concatenate([pts, -pts])
+    got = np.array([oracle.e4m3_encode(float(v)) for v in pts], np.uint8)
+    assert np.array_equal(got, _encode_torch(pts))
+
+
+def test_e4m3_encode_matches_torch_on_random_values():
+    g = np.random.default_rng(7)
+    mag = np.exp2(g.uniform(-12, np.log2(448.0), size=20000)).astype(np.float32)
+    x = np.where(g.random(20000) < 0.5, -mag, mag).astype(np.float32)
+    got = np.array([oracle.e4m3_encode(float(v)) for v in x], np.uint8)
+    assert np.array_equal(got, _encode_torch(x))
+
+
+# ----------------------------------------------------------------------------- router
+
+def sanitized(lg: np.ndarray) -> np.ndarray:
+    return np.nan_to_num(lg.astype(np.float32), nan=-FLT_MAX, posinf=FLT_MAX, neginf=-FLT_MAX)
+
+
+def test_router_ids_match_stable_argsort_on_nan_batch():
+    shape = golden("router_microbench_shape.json")
+    T, E, k = shape["tokens"], shape["experts"], shape["top_k"]
+    lg = synth.router_batch(T, E, k)
+    bits = synth.bf16_bits(lg)
+    v = sanitized(f32_of_bf16(lg))
+    ref = np.argsort(-v, axis=1, kind="stable")[:, :k]  # ties: lower index first
+    for scoring in ("softmax", "sigmoid"):
+        for renorm in (True, False):
+            ids, w = oracle.router_topk(bits, k, scoring, renorm)
+            assert np.array_equal(ids, ref)
+            assert all(len(set(r)) == k for r in ids.tolist())
+    # the 4 all-NaN rows pick experts 0..k-1 with softmax weights exactly 1/k
+    nan_rows = np.nonzero(np.isnan(f32_of_bf16(lg)).all(axis=1))[0]
+    assert len(nan_rows) == 4
+    ids, w = oracle.router_topk(bits, k, "softmax", True)
+    for r in nan_rows:
+        assert ids[r].tolist() == list(range(k))
+        assert np.all(w[r] == 1.0 / k)
+
+
+def test_router_nan_free_rows_unchanged_by_sanitising():
+    lg = f32_of_bf16(synth.router_batch())
+    ok = ~np.isnan(lg).any(axis=1)
+    ids, _ = oracle.router_topk(lg, 8)
+    raw = np.argsort(-lg[ok], axis=1, kind="stable")[:, :8]
+    assert ok.sum() > 0 and np.array_equal(ids[ok], raw)
+
+
+def test_router_k1_is_first_argmax():
+    g = np.random.default_rng(3)
+    lg = np.round(g.standard_normal((64, 40)) * 2).astype(np.float32)  # many exact ties
+    ids, _ = oracle.router_topk(lg, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(lg, axis=1))
+
+
+def test_router_softmax_weights_closed_form():
+    g = np.random.default_rng(4)
+    lg = g.standard_normal((50, 33)).astype(np.float32)
+    k = 5
+    ids, w = oracle.router_topk(lg, k, "softmax", True)
+    sel = np.take_along_axis(lg.astype(np.float64), ids, axis=1)
+    assert np.allclose(w, scipy.special.softmax(sel, axis=1), rtol=0, atol=1e-13)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-12)
+    ids2, w2 = oracle.router_topk(lg, k, "softmax", False)
+    full = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(w2, np.take_along_axis(full, ids2, axis=1), rtol=0, atol=1e-13)
+    assert np.all(np.diff(w, axis=1) <= 0)  # best first
+
+
+def test_router_sigmoid_weights_closed_form():
+    g = np.random.default_rng(5)
+    lg = g.standard_normal((50, 33)).astype(np.float32)
+    ids, w = oracle.router_topk(lg, 4, "sigmoid", False)
+    s = scipy.special.expit(np.take_along_axis(lg.astype(np.float64), ids, axis=1))
+    assert np.allclose(w, s, rtol=0, atol=1e-14)
+    ids, w = oracle.router_topk(lg, 4, "sigmoid", True)
+    assert np.allclose(w, s / s.sum(1, keepdims=True), rtol=0, atol=1e-14)
+
+
+def test_router_all_nan_sigmoid_and_unrenormalised_softmax():
+    lg = np.full((2, 10), np.nan, np.float32)
+    ids, w = oracle.router_topk(lg, 3, "sigmoid", True)
+    assert ids.tolist() == [[0, 1, 2]] * 2 and np.all(w == 1.0 / 3)
+    ids, w = oracle.router_topk(lg, 3, "sigmoid", False)
+    assert np.all(w == 0.0)
+    ids, w = oracle.router_topk(lg, 3, "softmax", False)
+    assert np.all(w == 1.0 / 10)
+
+
+def test_router_signed_zero_and_infinities():
+    lg = np.array([[-0.0, 0.0, -1.0, 0.0], [np.inf, 1.0, -np.inf, np.inf], [-np.inf] * 4], np.float32)
+    ids, w = oracle.router_topk(lg, 2)
+    assert ids.tolist() == [[0, 1], [0, 3], [0, 1]]
+    assert np.isfinite(w).all()
+    assert np.allclose(w[1], [0.5, 0.5]) and np.allclose(w[2], [0.5, 0.5])
+
+
+def test_router_k_equals_E_gives_every_expert_once():
+    g = np.random.default_rng(6)
+    lg = g.standard_normal((20, 9)).astype(np.float32)
+    ids, w = oracle.router_topk(lg, 9)
+    assert all(sorted(r) == list(range(9)) for r in ids.tolist())
+    assert np.allclose(w, np.take_along_axis(scipy.special.softmax(lg.astype(np.float64), 1), ids, 1), atol=1e-14)
+
+
+def test_router_logits_error_bound_and_exact_integers():
+    g = np.random.default_rng(8)
+    x = synth.to_bf16(g.standard_normal((6, 256)).astype(np.float32))
+    wr = synth.to_bf16((g.standard_normal((8, 256)) * 0.02).astype(np.float32))
+    got = oracle.router_logits(synth.bf16_bits(x), synth.bf16_bits(wr)).astype(np.float64)
+    xf, wf = x.double().numpy(), wr.double().numpy()
+    exact = xf @ wf.T  # products of bf16 values are exact in double; H=256 terms
+    u = 2.0 ** -24
+    gamma = 256 * u / (1 - 256 * u)
+    bound = gamma * (np.abs(xf) @ np.abs(wf).T)
+    assert np.all(np.abs(got - exact) <= bound)
+    xi = synth.to_bf16(g.integers(-3, 4, (5, 64)).astype(np.float32))
+    wi = synth.to_bf16(g.integers(-3, 4, (7, 64)).astype(np.float32))
+    gi = oracle.router_logits(synth.bf16_bits(xi), synth.bf16_bits(wi))
+    assert np.array_equal(gi, (xi.double() @ wi.double().T).numpy().astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- estimate and grouping
+
+def test_rows_per_expert_estimate_worked_example():
+    g = golden("rows_per_expert_h20.json")
+    T, k, E = g["tokens"], g["top_k"], g["physical_experts"]
+    assert T * k / E == pytest.approx(g["mean_rows_per_expert"])
+    assert oracle.rows_per_expert_estimate(T, k, E) == g["estimate"]
+    assert oracle.rows_per_expert_estimate(1, 8, 128) == 1
+    assert oracle.rows_per_expert_estimate(0, 8, 128) == 1
+    assert oracle.rows_per_expert_estimate(4096, 8, 128) == 256
+
+
+def _perm_reference(ids, E, ep_size, ep_rank):
+    El = E // ep_size
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    loc = flat - ep_rank * El
+    local = valid & (loc >= 0) & (loc < El)
+    key = np.where(local, loc, El)  # non-local last
+    order = np.argsort(key, kind="stable")
+    counts = np.bincount(loc[local], minlength=El)
+    return counts, order[: local.sum()], local, valid
+
+
+@pytest.mark.parametrize("T,k,E,ep_size,ep_rank", [(37, 3, 16, 1, 0), (200, 6, 400, 8, 3), (64, 8, 128, 1, 0),
+                                                   (1, 1, 1, 1, 0), (0, 4, 8, 1, 0), (50, 8, 8, 2, 1)])
+def test_route_permute_matches_stable_sort(T, k, E, ep_size, ep_rank):
+    g = np.random.default_rng(T * 1000 + k)
+    ids = g.integers(0, E, (T, k)).astype(np.int32)  # duplicates allowed here
+    r = oracle.route_permute(ids, E, ep_size, ep_rank)
+    counts, order, local, _ = _perm_reference(ids, E, ep_size, ep_rank)
+    assert np.array_equal(r["counts"], counts)
+    assert np.array_equal(r["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(r["perm_src"], order)
+    inv = r["inv_perm"]
+    assert np.all(inv[~local] == -1)
+    assert np.array_equal(inv[r["perm_src"]], np.arange(len(order)))  # inv o perm = id
+    if ep_size == 1:
+        assert r["counts"].sum() == T * k
+    # gather then scatter is the identity on the token rows
+    x = g.standard_normal((T, 5))
+    rows = x[r["perm_src"] // k] if k else x[:0]
+    back = np.zeros((T * k, 5))
+    back[r["perm_src"]] = rows
+    assert np.array_equal(back[local], np.repeat(x, k, axis=0)[local])
+
+
+def test_route_permute_drops_out_of_range_ids():
+    ids = np.array([[0, 9, -1], [3, 3, 7]], np.int32)
+    r = oracle.route_permute(ids, 8)
+    assert r["dropped"] == 2
+    assert r["counts"].tolist() == [1, 0, 0, 2, 0, 0, 0, 1]
+    assert r["perm_src"].tolist() == [0, 3, 4, 5]
+    assert r["inv_perm"].tolist() == [0, -1, -1, 1, 2, 3]
+
+
+# ----------------------------------------------------------------------------- FP8 activation quantisation
+
+def test_act_quant_matches_torch_route_and_amax_hits_448():
+    g = np.random.default_rng(9)
+    x = (g.standard_normal((9, 384)) * np.exp(g.uniform(-6, 6, (9, 1)))).astype(np.float32)
+    x[3, 128:256] = 0.0  # an all-zero group -> scale 1, codes 0
+    x[5, 7] = np.nan     # NaN clamps to +448
+    q, s = oracle.act_quant(x)
+    xt = torch.from_numpy(x).reshape(9, 3, 128)
+    amax = torch.nan_to_num(xt, nan=0.0).abs().amax(-1)
+    st = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    assert np.array_equal(s, st.numpy())
+    inv = 1.0 / st
+    y = (xt * inv[..., None]).clamp(-448, 448)
+    y = torch.where(torch.isnan(y), torch.full_like(y, 448.0), y)
+    qt = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(9, 384).numpy()
+    assert np.array_equal(q, qt)
+    assert q[5, 7] == 0x7E and s[3, 1] == 1.0 and np.all(q[3, 128:256] == 0)
+    for r in range(9):
+        for gi in range(3):
+            grp = x[r, gi * 128:(gi + 1) * 128]
+            if np.nanmax(np.abs(grp)) > 0 and not np.isnan(grp).any():
+                j = int(np.argmax(np.abs(grp)))
+                assert q[r, gi * 128 + j] & 0x7F == 0x7E
+
+
+def test_act_quant_error_bound():
+    g = np.random.default_rng(10)
+    x = g.standard_normal((4, 256)).astype(np.float32)
+    q, s = oracle.act_quant(x)
+    deq = np.array([[oracle.e4m3_decode(c) for c in row] for row in q], np.float64) * np.repeat(s, 128, axis=1)
+    # e4m3 keeps 4 significant bits: relative error <= 2^-4 for normals, absolute 2^-10*s below 2^-6*s
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * np.repeat(s, 128, axis=1)) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+# ----------------------------------------------------------------------------- layer
+
+def dense_swiglu(x, wg, wu, wd):
+    """torch float64: silu(x Wg^T) * (x Wu^T) then Wd^T, for one expert."""
+    return (torch.nn.functional.silu(x @ wg.T) * (x @ wu.T)) @ wd.T
+
+
+def test_single_expert_top1_is_dense_swiglu():
+    L = synth.tiny_layer(T=7, H=128, E=1, I=256)
+    ids = np.zeros((7, 1), np.int32)
+    w = np.ones((7, 1))
+    out = oracle.moe_tokens(synth.bf16_bits(L["x"]), ids, w, synth.bf16_bits(L["wg"]), synth.bf16_bits(L["wu"]),
+                            synth.bf16_bits(L["wd"]), E=1)
+    ref = dense_swiglu(L["x"].double(), L["wg"][0].double(), L["wu"][0].double(), L["wd"][0].double()).numpy()
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-13)
+
+
+def dense_mixture(x, gate, wg, wu, wd):
+    """out[t] = sum_e gate[t,e] * SwiGLU_e(x[t]), every expert evaluated on every token."""
+    ys = torch.stack([dense_swiglu(x, wg[e], wu[e], wd[e]) for e in range(wg.shape[0])], 1)  # [T,E,H]
+    return (gate[:, :, None] * ys).sum(1)
+
+
+@pytest.mark.parametrize("ep_size,ep_rank", [(1, 0), (2, 1), (4, 0)])
+def test_layer_matches_dense_gated_mixture(ep_size, ep_rank):
+    T, H, E, I, k = 16, 256, 8, 128, 2
+    L = synth.tiny_layer(T, H, E, I)
+    logits = oracle.router_logits(synth.bf16_bits(L["x"]), synth.bf16_bits(L["wr"]))
+    ids, w = oracle.router_topk(logits, k, "softmax", True)
+    El = E // ep_size
+    sl = slice(ep_rank * El, (ep_rank + 1) * El)
+    bits = {n: synth.bf16_bits(L[n][sl]) for n in ("wg", "wu", "wd")}
+    out = oracle.moe_tokens(synth.bf16_bits(L["x"]), ids, w, bits["wg"], bits["wu"], bits["wd"], E=E,
+                            ep_size=ep_size, ep_rank=ep_rank)
+    gate = np.zeros((T, E))
+    np.put_along_axis(gate, ids, w, axis=1)
+    gate = torch.from_numpy(gate[:, sl])
+    ref = dense_mixture(L["x"].double(), gate, L["wg"][sl].double(), L["wu"][sl].double(), L["wd"][sl].double())
+    assert np.allclose(out, ref.numpy(), rtol=1e-10, atol=1e-13)
+    if ep_size > 1:
+        no_local = ~np.any((ids >= ep_rank * El) & (ids < (ep_rank + 1) * El), axis=1)
+        assert np.all(out[no_local] == 0.0)
+
+
+def test_k_equals_E_is_dense_softmax_mixture():
+    T, H, E, I = 6, 128, 4, 128
+    L = synth.tiny_layer(T, H, E, I, seed=1)
+    g = np.random.default_rng(11)
+    lg = g.standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.router_topk(lg, E, "softmax", True)
+    out = oracle.moe_tokens(synth.bf16_bits(L["x"]), ids, w, *(synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")), E=E)
+    gate = torch.from_numpy(scipy.special.softmax(lg.astype(np.float64), axis=1))
+    ref = dense_mixture(L["x"].double(), gate, L["wg"].double(), L["wu"].double(), L["wd"].double())
+    assert np.allclose(out, ref.numpy(), rtol=1e-9, atol=1e-12)
+
+
+def test_layer_invariants_relabel_linearity_token_independence():
+    T, H, E, I, k = 12, 128, 6, 128, 3
+    L = synth.tiny_layer(T, H, E, I, seed=2)
+    g = np.random.default_rng(12)
+    lg = g.standard_normal((T, E)).astype(np.float32)
+    xb = synth.bf16_bits(L["x"])
+    wb = [synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")]
+    ids, w = oracle.router_topk(lg, k)
+    base = oracle.moe_tokens(xb, ids, w, *wb, E=E)
+    perm = g.permutation(E)  # new expert j is old expert perm[j]
+    ids2, w2 = oracle.router_topk(lg[:, perm], k)
+    out2 = oracle.moe_tokens(xb, ids2, w2, *(a[perm] for a in wb), E=E)
+    assert np.allclose(out2, base, rtol=1e-12, atol=1e-15)
+    wd2 = synth.bf16_bits(L["wd"] * 2)  # exact in bf16
+    assert np.array_equal(oracle.moe_tokens(xb, ids, w, wb[0], wb[1], wd2, E=E), 2 * base)
+    sub = np.array([3, 0, 11], np.int32)
+    assert np.array_equal(oracle.moe_tokens(xb, ids, w, *wb, E=E, tokens=sub), base[sub])
+    alone = oracle.moe_tokens(xb[5:6], ids[5:6], w[5:6], *wb, E=E)
+    assert np.array_equal(alone[0], base[5])
+
+
+def test_fp8_layer_matches_torch_dequantised_route():
+    T, H, E, I, k = 5, 256, 3, 256, 2
+    L = synth.tiny_layer(T, H, E, I, seed=3)
+    qg, sg = synth.block_quantize_fp8(L["wg"])
+    qu, su = synth.block_quantize_fp8(L["wu"])
+    qd, sd = synth.block_quantize_fp8(L["wd"])
+    g = np.random.default_rng(13)
+    ids, w = oracle.router_topk(g.standard_normal((T, E)).astype(np.float32), k)
+    out = oracle.moe_tokens(synth.bf16_bits(L["x"]), ids, w, qg.numpy(), qu.numpy(), qd.numpy(), E=E,
+                            sg=sg.numpy(), su=su.numpy(), sd=sd.numpy())
+
+    def deq(q, s):  # torch's e4m3 decode times the block scale
+        v = q.view(torch.float8_e4m3fn).double()
+        return v * s.double().repeat_interleave(128, 1).repeat_interleave(128, 2)
+
+    def quant_rows(a):  # per row, per 128 columns, through torch's fp32 ops and e4m3 cast
+        a = a.float().reshape(a.shape[0], -1, 128)
+        amax = a.abs().amax(-1, keepdim=True)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (a * (1.0 / s)).clamp(-448, 448).to(torch.float8_e4m3fn)
+        return (q.double() * s.double()).reshape(a.shape[0], -1)
+
+    Wg, Wu, Wd = deq(qg, sg), deq(qu, su), deq(qd, sd)
+    xq = quant_rows(L["x"].float())
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            a = torch.nn.functional.silu(xq[t] @ Wg[e].T) * (xq[t] @ Wu[e].T)
+            ref[t] += w[t, j] * (quant_rows(a[None].float())[0] @ Wd[e].T).numpy()
+    assert np.allclose(out, ref, rtol=1e-9, atol=1e-12)
+    # and the FP8 layer stays close to the bf16 layer it was quantised from
+    bf = oracle.moe_tokens(synth.bf16_bits(L["x"]), ids, w, *(synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")), E=E)
+    rel = np.abs(out - bf).max() / np.abs(bf).max()
+    assert rel < 0.15
+
+
+def test_duplicate_ids_become_two_rows():
+    T, H, E, I = 3, 128, 4, 128
+    L = synth.tiny_layer(T, H, E, I, seed=4)
+    xb = synth.bf16_bits(L["x"])
+    wb = [synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")]
+    ids = np.array([[2, 2], [1, 3], [0, 0]], np.int32)
+    w = np.array([[0.25, 0.75], [0.5, 0.5], [1.0, 1.0]])
+    out = oracle.moe_tokens(xb, ids, w, *wb, E=E)
+    one = oracle.moe_tokens(xb, np.array([[2], [1], [0]], np.int32), np.ones((3, 1)), *wb, E=E)
+    assert np.allclose(out[0], one[0], rtol=1e-14) and np.allclose(out[2], 2 * one[2], rtol=1e-14)
