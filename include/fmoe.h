@@ -1,0 +1,171 @@
+/*
+ * fmoe.h -- C ABI of libfmoe, a fused mixture-of-experts layer for AMD Instinct MI355X
+ * (gfx950): router top-k (softmax or sigmoid), per-expert grouping of the routed rows,
+ * grouped gate/up GEMM with SiLU-and-mul, grouped down GEMM (bf16 weights, or OCP e4m3
+ * weights with one fp32 scale per [128,128] block and per-token per-128-column activation
+ * scales), and the routing-weighted combine back to token order.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [H20]     "vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
+ *             Selection": paragraph 2 (a fused-experts entry point that takes expert-parallel
+ *             size and rank and FP8 block scales), paragraph 3 (workspace sized for the worst
+ *             case first; tile choice from rows per expert = ceil(tokens*top_k/experts) >= 1),
+ *             paragraph 4 (uniform and concentrated routing differ).
+ *   [PR39593] "PR #39593: [Bug]: Fix FlashInfer CUTLASS BF16 + CUDA graphs IMA": Root cause
+ *             (NaN logits made top-k repeat one id; repeated ids crashed the expert kernels;
+ *             the FP8 conversion clamps with fminf/fmaxf to +-448), Fix (NaN -> -FLT_MAX in the
+ *             router; K distinct ids), Test Plan (128x128 top-8 router micro-benchmark).
+ *   [LAB6]    "Lab notes #6: We tuned vLLM's MoE kernels on an H100 ...": intro (fp8_w8a8,
+ *             block_shape [128,128], E=128, N=768).
+ *
+ * Conventions for every entry point:
+ *   - All device pointers are plain device addresses; the caller allocates and owns every
+ *     buffer (inputs, outputs, weights, workspace).  The library allocates nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; none synchronises except fmoe_read_stats.
+ *   - All argument checks run on the host before anything is enqueued.  A failed check
+ *     returns its status and enqueues nothing.  A launch error returns FMOE_ERR_HIP.
+ *   - tokens == 0 returns FMOE_OK and launches nothing.
+ *   - Identical inputs give bitwise identical outputs (no order-dependent atomics).
+ *   - One workspace must not be used by two calls that run concurrently.
+ *   - Row-major layouts everywhere; "[A,B]" lists dimensions outermost first.
+ */
+#ifndef FMOE_H
+#define FMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FMOE_ABI_VERSION 1
+
+/* Limits of this build (checked, FMOE_ERR_UNSUPPORTED beyond them). */
+#define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
+#define FMOE_MAX_TOP_K 64         /* top_k                                                     */
+
+typedef enum {
+    FMOE_OK = 0,
+    FMOE_ERR_ARG = 1,          /* null pointer, misaligned pointer, inconsistent sizes   */
+    FMOE_ERR_UNSUPPORTED = 2,  /* a size or dtype outside the limits of this build       */
+    FMOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than fmoe_workspace_bytes              */
+    FMOE_ERR_HIP = 4           /* a HIP launch or runtime call failed                    */
+} fmoe_status;
+
+typedef enum { FMOE_BF16 = 0, FMOE_FP32 = 1, FMOE_FP8_E4M3 = 2 } fmoe_dtype; /* e4m3 = OCP E4M3FN, max 448 */
+typedef enum { FMOE_SOFTMAX = 0, FMOE_SIGMOID = 1 } fmoe_scoring;
+
+/* Shape of one layer call.
+ *   tokens  T >= 0        hidden H, inter I: positive multiples of 128
+ *   experts E (total physical expert slots, [H20] paragraph 3), 1 <= top_k <= min(E, 64)
+ *   ep_size divides E; this rank owns experts [ep_rank*E/ep_size, (ep_rank+1)*E/ep_size)
+ *   ([H20] paragraph 2); E_loc = E/ep_size <= 1024.
+ *   weight_dtype: FMOE_BF16 or FMOE_FP8_E4M3. */
+typedef struct {
+    int32_t tokens, hidden, inter, experts, top_k, ep_size, ep_rank;
+    int32_t weight_dtype;
+} fmoe_shape;
+
+/* Local expert weights, output features by rows, the reduction dimension contiguous:
+ *   gate, up [E_loc, I, H];  down [E_loc, H, I]   (bf16, or e4m3 codes one byte each)
+ *   FP8 only: gate_scale, up_scale [E_loc, I/128, H/128]; down_scale [E_loc, H/128, I/128]
+ *   (fp32 per [128,128] block, [H20] paragraph 2, [LAB6] intro).  bf16: all three NULL.
+ *   Weight pointers must be 16-byte aligned. */
+typedef struct {
+    const void *gate, *up, *down;
+    const float *gate_scale, *up_scale, *down_scale;
+} fmoe_weights;
+
+/* Counters the kernels leave in the workspace header (read with fmoe_read_stats). */
+typedef struct {
+    int64_t dropped_ids;     /* ids outside [0, E) seen by the grouping step (skipped)       */
+    int32_t local_rows;      /* R = rows of this rank's experts                              */
+    int32_t max_rows;        /* largest per-expert row count                                */
+    int32_t empty_experts;   /* local experts with no row                                   */
+    int32_t m_tiles;         /* row tiles of the grouped GEMMs                              */
+    int32_t rows_estimate;   /* host plan: max(1, ceil(T*top_k/E))                          */
+    int32_t tile_rows;       /* host plan: largest row tile of the grouped GEMMs            */
+} fmoe_stats;
+
+int fmoe_abi_version(void);
+const char* fmoe_status_string(int status);
+
+/* Bytes of workspace a call with this shape needs: the worst case over all routings (every
+ * assignment local, any per-expert imbalance), computed before any routing is known
+ * ([H20] paragraph 3).  Host only. */
+int fmoe_workspace_bytes(const fmoe_shape* shape, size_t* bytes);
+
+/* Router linear: logits[t,e] = sum_h x[t,h] * w_r[e,h] in fp32, one fused multiply-add per
+ * h in ascending h order starting from 0 (so the result is reproducible bit for bit).
+ *   x [T,H] bf16, w_r [E,H] bf16 -> logits [T,E] fp32.  H >= 1, E >= 1. */
+int fmoe_router_logits(const void* x, const void* w_r, int32_t T, int32_t H, int32_t E,
+                       float* logits, void* stream);
+
+/* Router top-k ([PR39593] Fix): each logit is read as fp32, NaN becomes -FLT_MAX and +-inf
+ * become +-FLT_MAX; experts are ordered by that value, larger first, lower index first
+ * among equals; the first k are written best first, always k distinct ids.
+ *   logits [T,E] (logits_dtype FMOE_BF16 or FMOE_FP32) -> topk_ids [T,k] int32,
+ *   topk_weights [T,k] fp32:
+ *     softmax: exp(v - max) / sum over all E, or over the k picks when renormalize != 0;
+ *     sigmoid: 1/(1+exp(-v)); renormalize != 0 divides by the sum of the k picks
+ *              (1/k each when that sum is 0). */
+int fmoe_router_topk(const void* logits, int32_t logits_dtype, int32_t T, int32_t E, int32_t k,
+                     int32_t scoring, int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+                     void* stream);
+
+/* Per-expert grouping of the T*k assignments topk_ids [T,k] for this rank (shape gives
+ * T, E, k, ep_size, ep_rank; H, I and weight_dtype are used only to size the workspace):
+ *   counts [E_loc]      rows per local expert
+ *   offsets [E_loc+1]   exclusive prefix sum of counts, offsets[E_loc] = R
+ *   perm_src [T*k]      first R entries: flat index t*k+j of each grouped row, experts
+ *                       ascending, flat index ascending inside an expert (stable)
+ *   inv_perm [T*k]      grouped row of each assignment, -1 when not local
+ * Ids outside [0,E) are skipped and counted (fmoe_read_stats); repeated ids in a token are
+ * legal and give separate rows.  ws/ws_bytes as for fmoe_experts. */
+int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Expert computation for given routing: out[t,:] = sum over j ascending with a local id of
+ *   topk_weights[t,j] * W_down[l] (silu(W_gate[l] x[t]) * (W_up[l] x[t])),  l = id - ep_rank*E_loc,
+ * computed as grouping -> (FP8: per-token per-128 e4m3 quantisation of x) -> grouped gate/up
+ * GEMM with fused SiLU-and-mul -> (FP8: quantisation of the activation) -> grouped down GEMM ->
+ * weighted combine in fp32, rounded once to bf16.  Tokens with no local id get zeros.
+ *   x [T,H] bf16 (16-byte aligned); topk_ids [T,k] int32; topk_weights [T,k] fp32;
+ *   out [T,H] bf16 (16-byte aligned); ws of at least fmoe_workspace_bytes(shape). */
+int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids,
+                 const float* topk_weights, const fmoe_weights* w, void* out,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Whole layer: fmoe_router_topk on logits [T,E] then fmoe_experts.  topk_ids_out [T,k] and
+ * topk_weights_out [T,k] receive the routing when not NULL (otherwise it stays in ws). */
+int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype,
+                 int32_t scoring, int32_t renormalize, const fmoe_weights* w, void* out,
+                 int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Stages of fmoe_forward, in launch order, for fmoe_forward_profiled. */
+enum {
+    FMOE_STAGE_ROUTER = 0, FMOE_STAGE_GROUP = 1, FMOE_STAGE_QUANT_X = 2, FMOE_STAGE_GEMM1 = 3,
+    FMOE_STAGE_QUANT_H = 4, FMOE_STAGE_GEMM2 = 5, FMOE_STAGE_COMBINE = 6, FMOE_NUM_STAGES = 7
+};
+
+/* fmoe_forward that also records stage_events[i] (hipEvent_t, created by the caller) on the
+ * stream just before stage i, and stage_events[FMOE_NUM_STAGES] after the last one; a stage
+ * that does not run for this dtype records its event pair back to back.  For timing. */
+int fmoe_forward_profiled(const fmoe_shape* shape, const void* x, const void* logits,
+                          int32_t logits_dtype, int32_t scoring, int32_t renormalize,
+                          const fmoe_weights* w, void* out, int32_t* topk_ids_out,
+                          float* topk_weights_out, void* ws, size_t ws_bytes, void* stream,
+                          void* const* stage_events);
+
+/* Copies the counters of the last call that used ws into *out.  Synchronises the stream:
+ * for tests and benchmarks, not for the hot path. */
+int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FMOE_H */

@@ -1,0 +1,335 @@
+// abi.cpp -- the extern "C" entry points of libfmoe: argument checks, the plan (rows per
+// expert estimate and tile size), worst-case workspace layout, and kernel launches.
+//
+// Plan ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
+// Selection", paragraph 3): the workspace is laid out for the worst case first (every
+// assignment local, any imbalance); then the rows-per-expert estimate
+// max(1, ceil(T*top_k/E)) with E the total physical expert slots picks the largest row tile
+// of the grouped GEMMs (16, 32, 64 or 128 rows).  The grouping kernel cuts each expert's real
+// row count into tiles of at most that size on the device, so concentrated routing gets
+// more tiles on its hot experts without a host round trip.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/fmoe.h"
+#include "launch.hpp"
+
+using namespace fmoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Worst-case workspace layout of one call.
+struct Layout {
+    size_t hdr, ids, wts, counts, offsets, perm, inv, rank, mtiles, xq, xs, h, hq, hs, y, total;
+};
+
+struct Plan {
+    int T, H, I, E, k, El, lo;
+    bool fp8;
+    long long n;         // T*k assignments
+    int rows_estimate;   // max(1, ceil(T*k/E))
+    int tile_rows;       // largest row tile: 16, 32, 64 or 128
+    int max_mtiles;      // bound on row tiles for any routing
+    Layout L;
+};
+
+int check_shape(const fmoe_shape* s) {
+    if (!s) return FMOE_ERR_ARG;
+    if (s->tokens < 0 || s->hidden <= 0 || s->inter <= 0 || s->experts <= 0 || s->top_k <= 0) return FMOE_ERR_ARG;
+    if (s->hidden % 128 || s->inter % 128) return FMOE_ERR_UNSUPPORTED;
+    if (s->top_k > s->experts) return FMOE_ERR_ARG;
+    if (s->top_k > FMOE_MAX_TOP_K) return FMOE_ERR_UNSUPPORTED;
+    if (s->ep_size <= 0 || s->experts % s->ep_size || s->ep_rank < 0 || s->ep_rank >= s->ep_size) return FMOE_ERR_ARG;
+    if (s->experts / s->ep_size > FMOE_MAX_EXPERTS || s->experts > FMOE_MAX_EXPERTS) return FMOE_ERR_UNSUPPORTED;
+    if (s->weight_dtype != FMOE_BF16 && s->weight_dtype != FMOE_FP8_E4M3) return FMOE_ERR_UNSUPPORTED;
+    if ((long long)s->tokens * s->top_k > INT_MAX / 2) return FMOE_ERR_UNSUPPORTED;
+    return FMOE_OK;
+}
+
+Plan make_plan(const fmoe_shape* s) {
+    Plan p;
+    p.T = s->tokens;
+    p.H = s->hidden;
+    p.I = s->inter;
+    p.E = s->experts;
+    p.k = s->top_k;
+    p.El = s->experts / s->ep_size;
+    p.lo = s->ep_rank * p.El;
+    p.fp8 = s->weight_dtype == FMOE_FP8_E4M3;
+    p.n = (long long)p.T * p.k;
+    long long est = (p.n + p.E - 1) / p.E;
+    p.rows_estimate = (int)(est < 1 ? 1 : est);
+    int tr = 16;
+    while (tr < p.rows_estimate && tr < 128) tr <<= 1;
+    p.tile_rows = tr;
+    // sum over experts of ceil(c_e / tile_rows) <= ceil(n / tile_rows) + (experts with a row),
+    // and no tile is empty
+    long long bound = (p.n + tr - 1) / tr + (p.El < p.n ? p.El : p.n);
+    if (bound > p.n) bound = p.n;
+    p.max_mtiles = (int)(bound < 1 ? 1 : bound);
+
+    Layout& L = p.L;
+    size_t o = 0;
+    const size_t n = (size_t)(p.n > 0 ? p.n : 1);
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.hdr = take(sizeof(DevHeader));
+    L.ids = take(n * 4);
+    L.wts = take(n * 4);
+    L.counts = take((size_t)p.El * 4);
+    L.offsets = take((size_t)(p.El + 1) * 4);
+    L.perm = take(n * 4);
+    L.inv = take(n * 4);
+    L.rank = take(n * 4);
+    L.mtiles = take((size_t)p.max_mtiles * sizeof(MTile));
+    if (p.fp8) {
+        L.xq = take((size_t)p.T * p.H);
+        L.xs = take((size_t)p.T * (p.H / 128) * 4);
+        L.h = take(n * p.I * 4);  // fp32 activation before its quantisation
+        L.hq = take(n * p.I);
+        L.hs = take(n * (p.I / 128) * 4);
+    } else {
+        L.xq = L.xs = L.hq = L.hs = 0;
+        L.h = take(n * p.I * 2);
+    }
+    L.y = take(n * p.H * 2);
+    L.total = o;
+    return p;
+}
+
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FMOE_OK : FMOE_ERR_HIP; }
+
+#define FMOE_TRY(expr)                          \
+    do {                                        \
+        hipError_t e_ = (expr);                 \
+        if (e_ != hipSuccess) return FMOE_ERR_HIP; \
+    } while (0)
+
+int check_weights(const Plan& p, const fmoe_weights* w) {
+    if (!w || !w->gate || !w->up || !w->down) return FMOE_ERR_ARG;
+    if (!aligned16(w->gate) || !aligned16(w->up) || !aligned16(w->down)) return FMOE_ERR_ARG;
+    const bool scales = w->gate_scale && w->up_scale && w->down_scale;
+    const bool none = !w->gate_scale && !w->up_scale && !w->down_scale;
+    if (p.fp8 ? !scales : !none) return FMOE_ERR_ARG;
+    return FMOE_OK;
+}
+
+void record(void* const* ev, int i, hipStream_t st) {
+    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], st);
+}
+
+// Grouping, expert GEMMs and combine for routing already in ids/wts (device pointers).
+int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* wts, const fmoe_weights* w, void* out,
+                char* ws, hipStream_t st, void* const* ev) {
+    const Layout& L = p.L;
+    DevHeader* hdr = (DevHeader*)(ws + L.hdr);
+    int32_t* perm = (int32_t*)(ws + L.perm);
+    int32_t* inv = (int32_t*)(ws + L.inv);
+    MTile* mtiles = (MTile*)(ws + L.mtiles);
+    const int cus = device_cus();
+
+    record(ev, FMOE_STAGE_GROUP, st);
+    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, (int32_t*)(ws + L.counts),
+                          (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), mtiles, hdr, st));
+
+    record(ev, FMOE_STAGE_QUANT_X, st);
+    if (p.fp8) FMOE_TRY(launch_quant_rows(x, true, p.T, p.H, (uint8_t*)(ws + L.xq), (float*)(ws + L.xs), nullptr, st));
+
+    record(ev, FMOE_STAGE_GEMM1, st);
+    GemmArgs g1;
+    g1.A = p.fp8 ? (const void*)(ws + L.xq) : x;
+    g1.A_scale = p.fp8 ? (const float*)(ws + L.xs) : nullptr;
+    g1.perm_src = perm;
+    g1.topk = p.k;
+    g1.W0 = w->gate;
+    g1.W1 = w->up;
+    g1.S0 = w->gate_scale;
+    g1.S1 = w->up_scale;
+    g1.N = p.I;
+    g1.K = p.H;
+    g1.out = ws + L.h;
+    g1.mtiles = mtiles;
+    g1.hdr = hdr;
+    FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.max_mtiles, cus, st));
+
+    record(ev, FMOE_STAGE_QUANT_H, st);
+    if (p.fp8)
+        FMOE_TRY(launch_quant_rows(ws + L.h, false, p.n, p.I, (uint8_t*)(ws + L.hq), (float*)(ws + L.hs), hdr, st));
+
+    record(ev, FMOE_STAGE_GEMM2, st);
+    GemmArgs g2;
+    g2.A = p.fp8 ? (const void*)(ws + L.hq) : (const void*)(ws + L.h);
+    g2.A_scale = p.fp8 ? (const float*)(ws + L.hs) : nullptr;
+    g2.perm_src = nullptr;
+    g2.topk = p.k;
+    g2.W0 = w->down;
+    g2.W1 = nullptr;
+    g2.S0 = w->down_scale;
+    g2.S1 = nullptr;
+    g2.N = p.H;
+    g2.K = p.I;
+    g2.out = ws + L.y;
+    g2.mtiles = mtiles;
+    g2.hdr = hdr;
+    FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.max_mtiles, cus, st));
+
+    record(ev, FMOE_STAGE_COMBINE, st);
+    FMOE_TRY(launch_combine(ws + L.y, inv, wts, p.T, p.k, p.H, out, st));
+    record(ev, FMOE_NUM_STAGES, st);
+    return FMOE_OK;
+}
+
+int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t logits_dtype, int32_t scoring,
+                 int32_t renormalize, const fmoe_weights* w, void* out, int32_t* ids_out, float* wts_out, void* ws,
+                 size_t ws_bytes, void* stream, void* const* ev) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (logits_dtype != FMOE_BF16 && logits_dtype != FMOE_FP32) return FMOE_ERR_UNSUPPORTED;
+    if (scoring != FMOE_SOFTMAX && scoring != FMOE_SIGMOID) return FMOE_ERR_ARG;
+    Plan p = make_plan(s);
+    if ((rc = check_weights(p, w))) return rc;
+    if (p.T == 0) return FMOE_OK;
+    if (!x || !logits || !out || !ws) return FMOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return FMOE_ERR_ARG;
+    if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    char* wsb = (char*)ws;
+    int32_t* ids = ids_out ? ids_out : (int32_t*)(wsb + p.L.ids);
+    float* wts = wts_out ? wts_out : (float*)(wsb + p.L.wts);
+    record(ev, FMOE_STAGE_ROUTER, st);
+    FMOE_TRY(launch_router_topk(logits, logits_dtype == FMOE_BF16, p.T, p.E, p.k, scoring, renormalize != 0, ids,
+                                wts, st));
+    return run_experts(p, x, ids, wts, w, out, wsb, st, ev);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fmoe_abi_version(void) { return FMOE_ABI_VERSION; }
+
+const char* fmoe_status_string(int status) {
+    switch (status) {
+        case FMOE_OK: return "ok";
+        case FMOE_ERR_ARG: return "invalid argument";
+        case FMOE_ERR_UNSUPPORTED: return "unsupported size or dtype";
+        case FMOE_ERR_WORKSPACE: return "workspace too small";
+        case FMOE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int fmoe_workspace_bytes(const fmoe_shape* shape, size_t* bytes) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!bytes) return FMOE_ERR_ARG;
+    *bytes = make_plan(shape).L.total;
+    return FMOE_OK;
+}
+
+int fmoe_router_logits(const void* x, const void* w_r, int32_t T, int32_t H, int32_t E, float* logits, void* stream) {
+    if (T < 0 || H <= 0 || E <= 0) return FMOE_ERR_ARG;
+    if (T == 0) return FMOE_OK;
+    if (!x || !w_r || !logits) return FMOE_ERR_ARG;
+    if ((long long)T * E > INT_MAX) return FMOE_ERR_UNSUPPORTED;
+    return hip_status(launch_router_logits(x, w_r, T, H, E, logits, (hipStream_t)stream));
+}
+
+int fmoe_router_topk(const void* logits, int32_t logits_dtype, int32_t T, int32_t E, int32_t k, int32_t scoring,
+                     int32_t renormalize, int32_t* topk_ids, float* topk_weights, void* stream) {
+    if (T < 0 || E <= 0 || k <= 0 || k > E) return FMOE_ERR_ARG;
+    if (E > FMOE_MAX_EXPERTS || k > FMOE_MAX_TOP_K) return FMOE_ERR_UNSUPPORTED;
+    if (logits_dtype != FMOE_BF16 && logits_dtype != FMOE_FP32) return FMOE_ERR_UNSUPPORTED;
+    if (scoring != FMOE_SOFTMAX && scoring != FMOE_SIGMOID) return FMOE_ERR_ARG;
+    if (T == 0) return FMOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return FMOE_ERR_ARG;
+    return hip_status(launch_router_topk(logits, logits_dtype == FMOE_BF16, T, E, k, scoring, renormalize != 0,
+                                         topk_ids, topk_weights, (hipStream_t)stream));
+}
+
+int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+                       int32_t* perm_src, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    Plan p = make_plan(shape);
+    if (p.T == 0) return FMOE_OK;
+    if (!topk_ids || !counts || !offsets || !perm_src || !inv_perm || !ws) return FMOE_ERR_ARG;
+    if (!aligned16(ws)) return FMOE_ERR_ARG;
+    if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
+    char* wsb = (char*)ws;
+    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, counts, offsets, perm_src,
+                                   inv_perm, (int32_t*)(wsb + p.L.rank), (MTile*)(wsb + p.L.mtiles),
+                                   (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
+}
+
+int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                 const fmoe_weights* w, void* out, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    Plan p = make_plan(shape);
+    if ((rc = check_weights(p, w))) return rc;
+    if (p.T == 0) return FMOE_OK;
+    if (!x || !topk_ids || !topk_weights || !out || !ws) return FMOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return FMOE_ERR_ARG;
+    if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
+    return run_experts(p, x, topk_ids, topk_weights, w, out, (char*)ws, (hipStream_t)stream, nullptr);
+}
+
+int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype, int32_t scoring,
+                 int32_t renormalize, const fmoe_weights* w, void* out, int32_t* topk_ids_out,
+                 float* topk_weights_out, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(shape, x, logits, logits_dtype, scoring, renormalize, w, out, topk_ids_out,
+                        topk_weights_out, ws, ws_bytes, stream, nullptr);
+}
+
+int fmoe_forward_profiled(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype,
+                          int32_t scoring, int32_t renormalize, const fmoe_weights* w, void* out,
+                          int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes, void* stream,
+                          void* const* stage_events) {
+    if (!stage_events) return FMOE_ERR_ARG;
+    return forward_impl(shape, x, logits, logits_dtype, scoring, renormalize, w, out, topk_ids_out,
+                        topk_weights_out, ws, ws_bytes, stream, stage_events);
+}
+
+int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {
+    if (!ws || !out) return FMOE_ERR_ARG;
+    DevHeader h;
+    hipStream_t st = (hipStream_t)stream;
+    if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess) return FMOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return FMOE_ERR_HIP;
+    std::memset(out, 0, sizeof(*out));
+    out->dropped_ids = h.dropped;
+    out->local_rows = h.local_rows;
+    out->max_rows = h.max_rows;
+    out->empty_experts = h.empty_experts;
+    out->m_tiles = h.m_tiles;
+    out->tile_rows = h.tile_rows;
+    out->rows_estimate = h.rows_estimate;
+    return FMOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// common.hpp -- device-side types and helpers shared by the libfmoe kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmoe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;  // largest finite OCP E4M3FN magnitude
+
+// Workspace header written by the grouping kernel and read by later kernels and by
+// fmoe_read_stats.  Field order is part of the workspace format of this library only.
+struct DevHeader {
+    int32_t m_tiles;        // row tiles of the grouped GEMMs
+    int32_t local_rows;     // R
+    int32_t max_rows;       // largest per-expert count
+    int32_t empty_experts;  // local experts with no row
+    long long dropped;      // ids outside [0, E)
+    int32_t tile_rows;      // largest rows per tile used to cut the experts
+    int32_t rows_estimate;  // max(1, ceil(T*top_k/E)) of the host plan
+    int32_t pad[8];
+};
+static_assert(sizeof(DevHeader) == 64, "header size");
+
+// One row tile of a grouped GEMM: local expert, first grouped row, number of rows.
+struct MTile {
+    int32_t expert, row0, rows, pad;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// fp32 -> OCP e4m3 code, round to nearest even with saturation (the gfx950 conversion
+// instruction; its rounding was checked against a software encoder on all 2^32 inputs
+// clamped to +-448).  Callers clamp to +-448 first.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        T w = __shfl_xor(v, o, 64);
+        v = v > w ? v : w;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace fmoe

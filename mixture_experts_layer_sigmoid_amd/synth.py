@@ -105,7 +105,7 @@ def routed_logits(config: int, T: int, E: int, k: int, routing: str = "uniform",
 
     uniform:      N(0,1).
     concentrated: N(0,1) + 16 on each token's chosen set.  round(hot_frac*T*k) assignments go
-                  to the experts 0..hot-1: every token takes floor(hot_total/T) of them and a
+                  to the experts 0..hot-1 (hot <= E - k): every token takes floor(hot_total/T) of them and a
                   seeded subset of tokens one more (never more than min(hot,k)); its remaining
                   picks are seeded distinct experts from hot..E-1."""
     base = rng(config, T, LOGITS, seed).standard_normal(size=(T, E), dtype=np.float32)
@@ -113,6 +113,9 @@ def routed_logits(config: int, T: int, E: int, k: int, routing: str = "uniform",
         return to_bf16(base)
     if routing != "concentrated":
         raise ValueError(routing)
+    hot = min(hot, E - k)  # leave k cold experts for every token
+    if hot < 1:
+        raise ValueError("concentrated routing needs E > top_k")
     g = rng(config, T, ROUTE, seed)
     total = int(round(hot_frac * T * k))
     per = np.full(T, total // T, np.int64)

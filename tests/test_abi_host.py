@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_sigmoid_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmoe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fmoe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fm.load_library()
+    names = declared_functions()
+    assert len(names) >= 10
+    assert set(names) == set(fm.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    lib = fm.load_library()
+    assert fm.fmoe_abi_version() == 1
+    text = open(HEADER).read()
+    assert "#define FMOE_ABI_VERSION 1" in text
+    for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")]:
+        assert word in lib.fmoe_status_string(code)
+
+
+def ws_bytes(**kw):
+    base = dict(tokens=16, hidden=256, inter=128, experts=8, top_k=2)
+    base.update(kw)
+    return fm.fmoe_workspace_bytes(fm.make_shape(**base))
+
+
+def test_workspace_bytes_worst_case_and_growth():
+    small = ws_bytes()
+    assert small > 0
+    # the Y buffer alone is T*k*H*2 bytes; the workspace holds at least that
+    assert ws_bytes(tokens=4096, hidden=2048, inter=768, experts=128, top_k=8) >= 4096 * 8 * 2048 * 2
+    assert ws_bytes(tokens=32) > ws_bytes(tokens=16)
+    # fp8 keeps fp32 activations and codes on top of the bf16 layout
+    assert ws_bytes(fp8=True) > 0
+    # the size does not depend on the expert-parallel rank
+    a = ws_bytes(tokens=288, hidden=7168, inter=2048, experts=400, top_k=6, ep_size=8, ep_rank=0, fp8=True)
+    b = ws_bytes(tokens=288, hidden=7168, inter=2048, experts=400, top_k=6, ep_size=8, ep_rank=7, fp8=True)
+    assert a == b
+    assert ws_bytes(tokens=0) > 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=200), fm.FMOE_ERR_UNSUPPORTED),      # not a multiple of 128
+    (dict(inter=100), fm.FMOE_ERR_UNSUPPORTED),
+    (dict(top_k=9), fm.FMOE_ERR_ARG),                 # k > E
+    (dict(top_k=0), fm.FMOE_ERR_ARG),
+    (dict(tokens=-1), fm.FMOE_ERR_ARG),
+    (dict(ep_size=3), fm.FMOE_ERR_ARG),               # does not divide E
+    (dict(ep_size=2, ep_rank=2), fm.FMOE_ERR_ARG),
+    (dict(experts=2048, top_k=2), fm.FMOE_ERR_UNSUPPORTED),
+    (dict(experts=128, top_k=65), fm.FMOE_ERR_UNSUPPORTED),
+])
+def test_workspace_bytes_rejects_bad_shapes(kw, code):
+    base = dict(tokens=16, hidden=256, inter=128, experts=8, top_k=2)
+    base.update(kw)
+    s = fm.make_shape(**base)
+    n = ctypes.c_size_t(0)
+    assert fm.load_library().fmoe_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == code
+
+
+def test_entry_points_reject_bad_arguments_without_a_device():
+    lib = fm.load_library()
+    s = fm.make_shape(16, 256, 128, 8, 2)
+    w = fm.fmoe_weights(0x1000, 0x2000, 0x3000, None, None, None)
+    ws_n = fm.fmoe_workspace_bytes(s)
+    P = ctypes.c_void_p
+    # null x
+    assert lib.fmoe_experts(ctypes.byref(s), None, P(0x100), P(0x200), ctypes.byref(w), P(0x300), P(0x400),
+                            ws_n, None) == fm.FMOE_ERR_ARG
+    # misaligned output
+    assert lib.fmoe_experts(ctypes.byref(s), P(0x100), P(0x100), P(0x200), ctypes.byref(w), P(0x308), P(0x400),
+                            ws_n, None) == fm.FMOE_ERR_ARG
+    # workspace too small
+    assert lib.fmoe_experts(ctypes.byref(s), P(0x100), P(0x100), P(0x200), ctypes.byref(w), P(0x300), P(0x400),
+                            ws_n - 1, None) == fm.FMOE_ERR_WORKSPACE
+    # bf16 weights must not carry scales; fp8 weights must
+    w_bad = fm.fmoe_weights(0x1000, 0x2000, 0x3000, 0x4000, None, None)
+    assert lib.fmoe_experts(ctypes.byref(s), P(0x100), P(0x100), P(0x200), ctypes.byref(w_bad), P(0x300),
+                            P(0x400), ws_n, None) == fm.FMOE_ERR_ARG
+    s8 = fm.make_shape(16, 256, 128, 8, 2, fp8=True)
+    assert lib.fmoe_experts(ctypes.byref(s8), P(0x100), P(0x100), P(0x200), ctypes.byref(w), P(0x300), P(0x400),
+                            fm.fmoe_workspace_bytes(s8), None) == fm.FMOE_ERR_ARG
+    # router: k > E, bad dtype, bad scoring
+    assert lib.fmoe_router_topk(P(0x100), 0, 4, 8, 9, 0, 1, P(0x200), P(0x300), None) == fm.FMOE_ERR_ARG
+    assert lib.fmoe_router_topk(P(0x100), 2, 4, 8, 2, 0, 1, P(0x200), P(0x300), None) == fm.FMOE_ERR_UNSUPPORTED
+    assert lib.fmoe_router_topk(P(0x100), 0, 4, 8, 2, 5, 1, P(0x200), P(0x300), None) == fm.FMOE_ERR_ARG
+    assert lib.fmoe_router_topk(P(0x100), 0, 4, 2000, 2, 0, 1, P(0x200), P(0x300), None) == fm.FMOE_ERR_UNSUPPORTED
+    # forward with unsupported logits dtype
+    assert lib.fmoe_forward(ctypes.byref(s), P(0x100), P(0x100), 7, 0, 1, ctypes.byref(w), P(0x300), None, None,
+                            P(0x400), ws_n, None) == fm.FMOE_ERR_UNSUPPORTED
+    # profiled forward needs its events
+    assert lib.fmoe_forward_profiled(ctypes.byref(s), P(0x100), P(0x100), 0, 0, 1, ctypes.byref(w), P(0x300), None,
+                                     None, P(0x400), ws_n, None, None) == fm.FMOE_ERR_ARG
+    # stats need a workspace
+    st = fm.fmoe_stats()
+    assert lib.fmoe_read_stats(None, None, ctypes.byref(st)) == fm.FMOE_ERR_ARG
+
+
+def test_zero_tokens_is_a_no_op():
+    lib = fm.load_library()
+    s = fm.make_shape(0, 256, 128, 8, 2)
+    w = fm.fmoe_weights(0x1000, 0x2000, 0x3000, None, None, None)
+    P = ctypes.c_void_p
+    assert lib.fmoe_experts(ctypes.byref(s), None, None, None, ctypes.byref(w), None, None, 0, None) == fm.FMOE_OK
+    assert lib.fmoe_forward(ctypes.byref(s), None, None, 0, 0, 1, ctypes.byref(w), None, None, None, None, 0,
+                            None) == fm.FMOE_OK
+    assert lib.fmoe_router_topk(None, 0, 0, 8, 2, 0, 1, None, None, None) == fm.FMOE_OK
+    assert lib.fmoe_router_logits(None, None, 0, 256, 8, None, None) == fm.FMOE_OK
+    assert lib.fmoe_route_permute(ctypes.byref(s), None, None, None, None, None, None, 0, None) == fm.FMOE_OK

@@ -1,0 +1,80 @@
+"""GPU parity of the per-expert grouping: counts, offsets, the stable permutation and its
+inverse bit-exact against the oracle; counters; determinism."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_sigmoid_amd as fm
+import oracle
+from mixture_experts_layer_sigmoid_amd import synth
+from gpu_common import announce
+
+pytestmark = pytest.mark.gpu
+
+
+def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
+    T, k = ids.shape
+    shape = fm.make_shape(T, H, I, E, k, ep_size, ep_rank)
+    r = fm.fmoe_route_permute(shape, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda())
+    ref = oracle.route_permute(ids, E, ep_size, ep_rank)
+    R = int(ref["offsets"][-1])
+    assert np.array_equal(r["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(r["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(r["perm_src"].cpu().numpy()[:R], ref["perm_src"])
+    assert np.array_equal(r["inv_perm"].cpu().numpy(), ref["inv_perm"])
+    st = fm.fmoe_read_stats(r["ws"])
+    assert st["local_rows"] == R
+    assert st["dropped_ids"] == ref["dropped"]
+    assert st["max_rows"] == int(ref["counts"].max(initial=0))
+    assert st["empty_experts"] == int((ref["counts"] == 0).sum())
+    est = max(1, -(-T * k // E))
+    assert st["rows_estimate"] == est
+    tr = st["tile_rows"]
+    assert tr in (16, 32, 64, 128) and (tr >= est or tr == 128)
+    assert st["m_tiles"] == int(sum(-(-c // tr) for c in ref["counts"]))
+    return r, ref
+
+
+@pytest.mark.parametrize("T,k,E,ep_size,ep_rank", [
+    (1, 1, 1, 1, 0), (1, 8, 128, 1, 0), (37, 3, 16, 1, 0), (64, 8, 128, 1, 0), (300, 4, 8, 1, 0),
+    (288, 6, 400, 8, 0), (288, 6, 400, 8, 5), (513, 8, 64, 4, 3), (4096, 8, 128, 1, 0), (2000, 2, 1024, 1, 0),
+])
+def test_group_random_ids_with_duplicates(T, k, E, ep_size, ep_rank):
+    announce(f"group T={T} k={k} E={E} ep={ep_size}/{ep_rank}")
+    g = np.random.default_rng(T * 7 + E)
+    ids = g.integers(0, E, (T, k)).astype(np.int32)  # repeated ids in a token are legal
+    check_group(ids, E, ep_size, ep_rank)
+
+
+def test_group_router_ids_full_sizes():
+    for cfg, T, E, k, routing, ep in [(3, 4096, 128, 8, "uniform", 1), (3, 4096, 128, 8, "concentrated", 1),
+                                      (5, 288, 400, 6, "uniform", 8), (5, 288, 400, 6, "concentrated", 8)]:
+        announce(f"group router ids T={T} E={E} k={k} {routing} ep={ep}")
+        lg = synth.routed_logits(cfg, T, E, k, routing)
+        ids, _ = oracle.router_topk(synth.bf16_bits(lg), k)
+        r, ref = check_group(ids, E, ep, 0)
+        if routing == "concentrated":
+            hot = ref["counts"][:8].sum()
+            assert hot >= 0.85 * T * k
+
+
+def test_group_all_tokens_one_expert_and_out_of_range():
+    announce("group all tokens to one expert, out-of-range ids")
+    T, k, E = 200, 6, 32
+    check_group(np.zeros((T, k), np.int32), E)
+    g = np.random.default_rng(3)
+    ids = g.integers(-5, E + 5, (T, k)).astype(np.int32)
+    check_group(ids, E)
+    check_group(ids, E, 4, 2)
+
+
+def test_group_is_deterministic():
+    announce("group determinism")
+    T, k, E = 4096, 8, 128
+    ids = torch.from_numpy(np.random.default_rng(5).integers(0, E, (T, k)).astype(np.int32)).cuda()
+    shape = fm.make_shape(T, 2048, 768, E, k)
+    first = fm.fmoe_route_permute(shape, ids)
+    for _ in range(10):
+        again = fm.fmoe_route_permute(shape, ids)
+        for key in ("counts", "offsets", "perm_src", "inv_perm"):
+            assert torch.equal(again[key], first[key])
