@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+Headline step: one fmoe_forward call (router top-k -> grouping -> gate/up GEMM with
+SiLU-and-mul -> down GEMM -> weighted combine) on the bf16 layer H=2048, I=768, E=128,
+top-8 (the 30B-total / 3B-active expert shape) at T=256 tokens with uniform routing from
+N(0,1) logits.  Inputs and weights are resident in HBM before timing starts.  Every step
+uses another seeded batch, and the weights rotate over several copies in HBM, so a step
+cannot find the expert weights it needs in the 256 MB Infinity Cache left over from the
+previous step (each call reads them from HBM, as in a model where other layers run between
+two calls of this one).
+
+value = HBM TB/s on the touched expert weights (bytes of the experts the routing used /
+wall time per step).  ms_per_step is the wall time per call.  Stage times come from HIP
+events the library records on its stream between the stages (fmoe_forward_profiled).
+
+Also reported: a sweep over T = 1..4096 (uniform and concentrated routing), the FP8 w8a8
+layer at T = 64/128/256, and the FP8 expert-parallel shard (T=288, top-6 of 400 slots, the
+50 local experts of rank 0) uniform and concentrated; the roofline of the dominant kernel;
+and the CPU oracle timed on a bounded sample of the headline batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE µs/call + HBM TB/s on touched weights (T=1..4096), uniform & skewed"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+CACHE_BYTES = 256 << 20  # Infinity Cache (MALL)
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+class Workload:
+    def __init__(self, name, *, config, T, H, I, E, k, fp8=False, routing="uniform", ep_size=1, ep_rank=0,
+                 weight_config=None):
+        self.name, self.config, self.T, self.H, self.I, self.E, self.k = name, config, T, H, I, E, k
+        self.fp8, self.routing, self.ep_size, self.ep_rank = fp8, routing, ep_size, ep_rank
+        self.weight_config = config if weight_config is None else weight_config
+        self.El = E // ep_size
+
+    @property
+    def dtype(self):
+        return "fp8" if self.fp8 else "bf16"
+
+    def expert_bytes(self):
+        """Weight bytes of one expert (gate + up + down, plus fp32 block scales for FP8)."""
+        elems = 3 * self.H * self.I
+        if self.fp8:
+            return elems + 3 * (self.H // 128) * (self.I // 128) * 4
+        return 2 * elems
+
+    def gemm1_bytes_per_expert(self):
+        elems = 2 * self.H * self.I
+        return elems + 2 * (self.H // 128) * (self.I // 128) * 4 if self.fp8 else 2 * elems
+
+    def describe(self):
+        return dict(workload=self.name, tokens=self.T, hidden=self.H, inter=self.I, experts=self.E, top_k=self.k,
+                    ep_size=self.ep_size, ep_rank=self.ep_rank, local_experts=self.El, weights=self.dtype,
+                    routing=self.routing)
+
+
+def build_inputs(wl: Workload, n_batches: int, n_copies: int):
+    import torch
+
+    import mixture_experts_layer_sigmoid_amd as fm
+    from mixture_experts_layer_sigmoid_amd import synth
+
+    dev = torch.device("cuda:0")
+    if wl.fp8:
+        base = [t.to(dev) for t in synth.expert_weights_fp8(wl.weight_config, wl.El, wl.H, wl.I, wl.ep_rank * wl.El)]
+    else:
+        base = [t.to(dev) for t in synth.expert_weights_bf16(wl.weight_config, wl.El, wl.H, wl.I, wl.ep_rank * wl.El)]
+    copies = [fm.ExpertWeights(*base)] + [fm.ExpertWeights(*[t.clone() for t in base]) for _ in range(n_copies - 1)]
+    batches = []
+    for b in range(n_batches):
+        x = synth.activations(wl.config, wl.T, wl.H, seed=b).to(dev)
+        lg = synth.routed_logits(wl.config, wl.T, wl.E, wl.k, wl.routing, seed=b).to(dev)
+        batches.append((x, lg))
+    shape = fm.make_shape(wl.T, wl.H, wl.I, wl.E, wl.k, wl.ep_size, wl.ep_rank, wl.fp8)
+    ws = fm.workspace(shape, dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    return shape, copies, batches, ws, out
+
+
+def pct(v, q):
+    s = sorted(v)
+    i = min(len(s) - 1, max(0, int(math.ceil(q / 100.0 * len(s))) - 1))
+    return s[i]
+
+
+def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None):
+    """warmup + steps timed calls, back to back; returns the wall time per call, per-call times
+    from a start/end event pair (or, with `dominant`, the live duration of that stage from the
+    event pair around it), a separate untimed pass with every stage event, and the routing
+    counters of every batch."""
+    import torch
+
+    import mixture_experts_layer_sigmoid_amd as fm
+
+    touched_guess = wl.El * (1 - (1 - wl.k / wl.E) ** wl.T) * wl.expert_bytes()
+    n_copies = max(2, min(8, int(math.ceil(2 * CACHE_BYTES / max(touched_guess, 1))) + 1))
+    n_batches = max(4, n_copies)
+    shape, copies, batches, ws, out = build_inputs(wl, n_batches, n_copies)
+
+    # routing counters of each batch (read once, outside the timed region)
+    stats = []
+    for b in range(n_batches):
+        fm.fmoe_forward(shape, batches[b][0], batches[b][1], copies[0], ws=ws, out=out)
+        stats.append(fm.fmoe_read_stats(ws))
+
+    NS = fm.FMOE_NUM_STAGES
+    if dominant is None:
+        pair = (0, NS)
+    else:
+        s = fm.STAGES.index(dominant)
+        pair = (s, s + 1)
+    ev = []
+    for _ in range(steps):
+        e = [None] * (NS + 1)
+        e[pair[0]] = torch.cuda.Event(enable_timing=True)
+        e[pair[1]] = torch.cuda.Event(enable_timing=True)
+        ev.append(e)
+
+    def call(j, events=None):
+        x, lg = batches[j % n_batches]
+        fm.fmoe_forward(shape, x, lg, copies[j % n_copies], ws=ws, out=out, stage_events=events)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    pair_us = [ev[i][pair[0]].elapsed_time(ev[i][pair[1]]) * 1e3 for i in range(steps)]
+
+    # stage breakdown: a separate pass with every event (each record adds a little time)
+    full = [[torch.cuda.Event(enable_timing=True) for _ in range(NS + 1)] for _ in range(steps)]
+    for i in range(steps):
+        call(warmup + steps + i, full[i])
+    torch.cuda.synchronize()
+    stage_us = {name: sum(full[i][s].elapsed_time(full[i][s + 1]) for i in range(steps)) * 1e3 / steps
+                for s, name in enumerate(fm.STAGES)}
+
+    used = [stats[(warmup + i) % n_batches] for i in range(steps)]
+    touched = sum(wl.El - u["empty_experts"] for u in used) / steps
+    rows = sum(u["local_rows"] for u in used) / steps
+    max_rows = max(u["max_rows"] for u in used)
+    del copies, batches, ws, out
+    torch.cuda.empty_cache()
+    return dict(wall_s=wall, pair_us=pair_us, dominant=dominant, stage_us=stage_us, touched=touched, rows=rows,
+                max_rows=max_rows, rows_estimate=used[0]["rows_estimate"], tile_rows=used[0]["tile_rows"],
+                copies=n_copies)
+
+
+def summarize(wl: Workload, m: dict) -> dict:
+    call_us = m["pair_us"] if m["dominant"] is None else [m["wall_s"] * 1e6]
+    p50 = pct(call_us, 50)
+    tb = m["touched"] * wl.expert_bytes()
+    flops = 6.0 * m["rows"] * wl.H * wl.I
+    return dict(**wl.describe(), us_p20=round(pct(call_us, 20), 2), us_p50=round(p50, 2),
+                us_p80=round(pct(call_us, 80), 2), us_wall=round(m["wall_s"] * 1e6, 2),
+                touched_experts=round(m["touched"], 2), touched_MB=round(tb / 1e6, 1),
+                hbm_TBps=round(tb / (p50 * 1e-6) / 1e12, 3), tokens_per_s=round(wl.T / (p50 * 1e-6), 1),
+                mfma_util=round(flops / (p50 * 1e-6) / (MFMA_PEAK_TFLOPS[wl.dtype] * 1e12), 4),
+                rows_estimate=m["rows_estimate"], tile_rows=m["tile_rows"], max_rows=m["max_rows"],
+                stages_us={k: round(v, 2) for k, v in m["stage_us"].items()})
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "mixture_experts_layer_sigmoid_amd", "csrc", "gemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload_name: str, stage: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        ent = rec.get(workload_name, {}).get(stage)
+        if not ent or ent.get("kernel_sha") != kernel_hash():
+            return None
+        return ent.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
+    """The CPU oracle (as it stands) on a bounded token sample of batch 0 of the workload."""
+    import numpy as np
+
+    import oracle
+    from mixture_experts_layer_sigmoid_amd import synth
+
+    x = synth.activations(wl.config, wl.T, wl.H, seed=0)
+    lg = synth.routed_logits(wl.config, wl.T, wl.E, wl.k, wl.routing, seed=0)
+    t0 = time.perf_counter()
+    ids, w = oracle.router_topk(synth.bf16_bits(lg), wl.k)
+    route_s = time.perf_counter() - t0
+    wg, wu, wd = (synth.bf16_bits(t) for t in synth.expert_weights_bf16(wl.weight_config, wl.El, wl.H, wl.I))
+    xb = synth.bf16_bits(x)
+    threads = oracle.num_threads()
+    done, spent, n = 0, 0.0, max(threads, 8)
+    while spent < target_s and done < wl.T:
+        tok = np.arange(done, min(wl.T, done + n), dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.moe_tokens(xb, ids, w, wg, wu, wd, E=wl.E, tokens=tok)
+        spent += time.perf_counter() - t0
+        done += len(tok)
+        n *= 2
+    per_call = spent / done * wl.T + route_s
+    touched = len(np.unique(ids)) * wl.expert_bytes()
+    return dict(value=round(touched / per_call / 1e12, 6), unit="TB/s", cores=threads, kind="oracle",
+                us_per_call=round(per_call * 1e6, 1),
+                sample=f"{done} of {wl.T} tokens of batch 0 ({spent:.1f} s of expert work, router on all "
+                       f"{wl.T} tokens), extrapolated to the whole call; double-precision C oracle, "
+                       f"OpenMP over tokens, {threads} threads on {platform.processor() or platform.machine()}")
+
+
+def host_cpu():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true", help="headline step only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep-steps", type=int, default=12)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this layer runs on a single MI355X (no collectives); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_sigmoid_amd as fm
+    from mixture_experts_layer_sigmoid_amd import synth
+
+    fm.load_library()
+    torch.cuda.init()
+    B3 = synth.BF16_LAYER
+    head = Workload("bf16 H2048 I768 E128 top8, T=256, uniform", config=B3, T=256, H=2048, I=768, E=128, k=8)
+    print(f"[bench] headline: {head.name}", file=sys.stderr, flush=True)
+    # the gate/up GEMM streams two thirds of the touched weight bytes: the dominant kernel
+    dom = "gemm1"
+    m = measure(head, args.steps, args.warmup, dominant=dom)
+    hs = summarize(head, m)
+    touched_bytes = m["touched"] * head.expert_bytes()
+    value = touched_bytes / m["wall_s"] / 1e12
+
+    # algorithmic bytes of one gate/up launch: the touched experts' gate and up weights, the
+    # gathered activation rows it reads and the activation it writes
+    alg = m["touched"] * head.gemm1_bytes_per_expert() + m["rows"] * (head.H + head.I) * 2
+    dom_us = sum(m["pair_us"]) / len(m["pair_us"])
+    achieved = alg / (dom_us * 1e-6) / 1e9
+    roof = dict(kernel="k_grouped_gemm (gate/up, SiLU-and-mul)", bound="hbm", achieved=round(achieved, 1),
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                traffic=traffic_from_profile(head.name, dom), algorithmic_bytes_per_launch=int(alg),
+                avg_launch_us=round(dom_us, 2), stage_breakdown_us={k: round(v, 2) for k, v in m["stage_us"].items()})
+
+    sweep = [hs]
+    if not args.no_sweep:
+        work = []
+        for T in (1, 8, 32, 128, 256, 512, 1024, 4096):
+            for routing in ("uniform", "concentrated"):
+                if T == 256 and routing == "uniform":
+                    continue
+                if T == 1 and routing == "concentrated":
+                    continue
+                work.append(Workload(f"bf16 H2048 I768 E128 top8, T={T}, {routing}", config=B3, T=T, H=2048, I=768,
+                                     E=128, k=8, routing=routing))
+        for T in (64, 128, 256):
+            work.append(Workload(f"fp8 w8a8 H2048 I768 E128 top8, T={T}, uniform", config=synth.FP8_LAYER,
+                                 weight_config=B3, T=T, H=2048, I=768, E=128, k=8, fp8=True))
+        for routing in ("uniform", "concentrated"):
+            work.append(Workload(f"fp8 shard H7168 I2048 top6 of 400 (ep 8, 50 local), T=288, {routing}",
+                                 config=synth.EP_SHARD, T=288, H=7168, I=2048, E=400, k=6, fp8=True, routing=routing,
+                                 ep_size=8, ep_rank=0))
+        for wl in work:
+            print(f"[bench] sweep: {wl.name}", file=sys.stderr, flush=True)
+            sweep.append(summarize(wl, measure(wl, args.sweep_steps, 3)))
+            print(f"[bench]   p50 {sweep[-1]['us_p50']} us, {sweep[-1]['hbm_TBps']} TB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(head)
+
+    line = dict(metric=METRIC, value=round(value, 4), unit="TB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=round(m["wall_s"] * 1e3, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="bf16", data="synthetic",
+                config=dict(**head.describe(), us_per_call=round(m["wall_s"] * 1e6, 2),
+                            tokens_per_s=round(head.T / m["wall_s"], 1),
+                            mfma_util=round(6.0 * m["rows"] * head.H * head.I / m["wall_s"] / 2.5e15, 4),
+                            weight_copies=m["copies"]),
+                roofline=roof, cpu_baseline=cpu, host_cpu=host_cpu(), kernel_sha=kernel_hash(),
+                sweep=sweep)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

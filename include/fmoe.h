@@ -45,6 +45,7 @@ extern "C" {
 /* Limits of this build (checked, FMOE_ERR_UNSUPPORTED beyond them). */
 #define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
 #define FMOE_MAX_TOP_K 64         /* top_k                                                     */
+#define FMOE_MAX_DIM 65536        /* hidden and inter                                          */
 
 typedef enum {
     FMOE_OK = 0,
@@ -58,7 +59,7 @@ typedef enum { FMOE_BF16 = 0, FMOE_FP32 = 1, FMOE_FP8_E4M3 = 2 } fmoe_dtype; /* 
 typedef enum { FMOE_SOFTMAX = 0, FMOE_SIGMOID = 1 } fmoe_scoring;
 
 /* Shape of one layer call.
- *   tokens  T >= 0        hidden H, inter I: positive multiples of 128
+ *   tokens  T >= 0        hidden H, inter I: positive multiples of 128, at most 65536
  *   experts E (total physical expert slots, [H20] paragraph 3), 1 <= top_k <= min(E, 64)
  *   ep_size divides E; this rank owns experts [ep_rank*E/ep_size, (ep_rank+1)*E/ep_size)
  *   ([H20] paragraph 2); E_loc = E/ep_size <= 1024.
@@ -154,7 +155,8 @@ enum {
 
 /* fmoe_forward that also records stage_events[i] (hipEvent_t, created by the caller) on the
  * stream just before stage i, and stage_events[FMOE_NUM_STAGES] after the last one; a stage
- * that does not run for this dtype records its event pair back to back.  For timing. */
+ * that does not run for this dtype records its event pair back to back.  NULL entries are
+ * skipped (each recorded event adds a few microseconds to the stream).  For timing. */
 int fmoe_forward_profiled(const fmoe_shape* shape, const void* x, const void* logits,
                           int32_t logits_dtype, int32_t scoring, int32_t renormalize,
                           const fmoe_weights* w, void* out, int32_t* topk_ids_out,

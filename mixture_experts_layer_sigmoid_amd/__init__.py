@@ -221,8 +221,9 @@ def fmoe_forward(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: Ex
                  out: torch.Tensor | None = None, return_routing: bool = False, stage_events=None):
     """Whole layer -> out [T,H] bf16 (and (ids, weights) when return_routing).
 
-    stage_events: optional list of FMOE_NUM_STAGES+1 torch.cuda.Event(enable_timing=True);
-    when given, fmoe_forward_profiled records them around the stages."""
+    stage_events: optional list of FMOE_NUM_STAGES+1 entries, each a
+    torch.cuda.Event(enable_timing=True) or None; when given, fmoe_forward_profiled records
+    the events around the stages (None entries are skipped)."""
     _dev(x, "x", torch.bfloat16)
     _dev(logits, "logits")
     dev = x.device
@@ -242,9 +243,10 @@ def fmoe_forward(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: Ex
         if len(stage_events) != FMOE_NUM_STAGES + 1:
             raise ValueError("stage_events needs FMOE_NUM_STAGES + 1 events")
         for e in stage_events:  # torch creates the underlying hipEvent lazily
-            if e.cuda_event == 0:
+            if e is not None and e.cuda_event == 0:
                 e.record()
-        handles = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
+        handles = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event if e is not None else None
+                                                          for e in stage_events])
         _check("fmoe_forward_profiled", lib.fmoe_forward_profiled(*args, handles))
     return (out, ids, wts) if return_routing else out
 

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -29,7 +30,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Worst-case workspace layout of one call.
 struct Layout {
-    size_t hdr, ids, wts, counts, offsets, perm, inv, rank, mtiles, xq, xs, h, hq, hs, y, total;
+    size_t hdr, ids, wts, counts, offsets, perm, inv, rank, grp, mtiles, xq, xs, h, hq, hs, y, total;
 };
 
 struct Plan {
@@ -39,6 +40,7 @@ struct Plan {
     int rows_estimate;   // max(1, ceil(T*k/E))
     int tile_rows;       // largest row tile: 16, 32, 64 or 128
     int max_mtiles;      // bound on row tiles for any routing
+    int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
     Layout L;
 };
 
@@ -46,6 +48,7 @@ int check_shape(const fmoe_shape* s) {
     if (!s) return FMOE_ERR_ARG;
     if (s->tokens < 0 || s->hidden <= 0 || s->inter <= 0 || s->experts <= 0 || s->top_k <= 0) return FMOE_ERR_ARG;
     if (s->hidden % 128 || s->inter % 128) return FMOE_ERR_UNSUPPORTED;
+    if (s->hidden > FMOE_MAX_DIM || s->inter > FMOE_MAX_DIM) return FMOE_ERR_UNSUPPORTED;
     if (s->top_k > s->experts) return FMOE_ERR_ARG;
     if (s->top_k > FMOE_MAX_TOP_K) return FMOE_ERR_UNSUPPORTED;
     if (s->ep_size <= 0 || s->experts % s->ep_size || s->ep_rank < 0 || s->ep_rank >= s->ep_size) return FMOE_ERR_ARG;
@@ -68,9 +71,26 @@ Plan make_plan(const fmoe_shape* s) {
     p.n = (long long)p.T * p.k;
     long long est = (p.n + p.E - 1) / p.E;
     p.rows_estimate = (int)(est < 1 ? 1 : est);
+    // Largest row tile: the estimate plus three standard deviations of the per-expert count
+    // under uniform routing (about sqrt(estimate)), so a uniform batch rarely cuts an expert
+    // in two; heavier experts get more tiles on the device.
+    const double need = p.rows_estimate + 3.0 * std::sqrt((double)p.rows_estimate) + 1.0;
     int tr = 16;
-    while (tr < p.rows_estimate && tr < 128) tr <<= 1;
+    while (tr < need && tr < 128) tr <<= 1;
+    // FP8 stages the tile's activation scales in LDS: keep them within 64 KB
+    while (p.fp8 && tr > 16 && gemm_lds_bytes(true, p.H > p.I ? p.H : p.I, tr) > 65536) tr >>= 1;
     p.tile_rows = tr;
+    // Split the reduction over 2 or 4 wavefronts when the expected tiles (about one per
+    // active expert under uniform routing) times the 16-feature blocks leave the GPU's
+    // 1024 SIMDs with fewer than two wavefronts each.
+    const long long local_rows = (p.n * p.El + p.E - 1) / p.E;
+    const long long active = local_rows < p.El ? local_rows : p.El;
+    auto pick_wk = [&](int N) {
+        const long long tasks = active * (N / 16);
+        return tasks < 1024 ? 4 : (tasks < 2048 ? 2 : 1);
+    };
+    p.wk1 = pick_wk(p.I);
+    p.wk2 = pick_wk(p.H);
     // sum over experts of ceil(c_e / tile_rows) <= ceil(n / tile_rows) + (experts with a row),
     // and no tile is empty
     long long bound = (p.n + tr - 1) / tr + (p.El < p.n ? p.El : p.n);
@@ -93,6 +113,7 @@ Plan make_plan(const fmoe_shape* s) {
     L.perm = take(n * 4);
     L.inv = take(n * 4);
     L.rank = take(n * 4);
+    L.grp = take(group_scratch_bytes((long long)n, p.El));
     L.mtiles = take((size_t)p.max_mtiles * sizeof(MTile));
     if (p.fp8) {
         L.xq = take((size_t)p.T * p.H);
@@ -139,7 +160,7 @@ int check_weights(const Plan& p, const fmoe_weights* w) {
 }
 
 void record(void* const* ev, int i, hipStream_t st) {
-    if (ev) (void)hipEventRecord((hipEvent_t)ev[i], st);
+    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], st);
 }
 
 // Grouping, expert GEMMs and combine for routing already in ids/wts (device pointers).
@@ -154,7 +175,8 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
 
     record(ev, FMOE_STAGE_GROUP, st);
     FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, (int32_t*)(ws + L.counts),
-                          (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), mtiles, hdr, st));
+                          (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
+                          hdr, st));
 
     record(ev, FMOE_STAGE_QUANT_X, st);
     if (p.fp8) FMOE_TRY(launch_quant_rows(x, true, p.T, p.H, (uint8_t*)(ws + L.xq), (float*)(ws + L.xs), nullptr, st));
@@ -174,7 +196,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g1.out = ws + L.h;
     g1.mtiles = mtiles;
     g1.hdr = hdr;
-    FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.max_mtiles, cus, st));
+    FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_mtiles, cus, st));
 
     record(ev, FMOE_STAGE_QUANT_H, st);
     if (p.fp8)
@@ -195,7 +217,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g2.out = ws + L.y;
     g2.mtiles = mtiles;
     g2.hdr = hdr;
-    FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.max_mtiles, cus, st));
+    FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.wk2, p.max_mtiles, cus, st));
 
     record(ev, FMOE_STAGE_COMBINE, st);
     FMOE_TRY(launch_combine(ws + L.y, inv, wts, p.T, p.k, p.H, out, st));
@@ -281,9 +303,9 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
     if (!aligned16(ws)) return FMOE_ERR_ARG;
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
     char* wsb = (char*)ws;
-    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, counts, offsets, perm_src,
-                                   inv_perm, (int32_t*)(wsb + p.L.rank), (MTile*)(wsb + p.L.mtiles),
-                                   (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
+    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, counts, offsets,
+                                   perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp),
+                                   (MTile*)(wsb + p.L.mtiles), (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
 }
 
 int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids, const float* topk_weights,

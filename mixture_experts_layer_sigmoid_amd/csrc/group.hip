@@ -1,51 +1,89 @@
 // group.hip -- per-expert grouping of the routed rows and the row-tile list of the grouped
-// GEMMs, in one workgroup.
+// GEMMs.
 //
-// The flat assignments i = t*k + j are cut into 8 contiguous segments, one per wavefront.
-// Phase 1: each wavefront walks its segment 64 assignments at a time, in order; the lanes
-// that hold the same local expert find each other with ballots, so every assignment gets
-// its rank among the earlier ones of its expert in the segment (a running count per
-// (wavefront, expert) in LDS).  Phase 2: a scan per expert over the 8 segments and a scan
-// over experts give each (segment, expert) its first grouped row, the counts and offsets,
-// and the row tiles.  Phase 3: every assignment is written to its grouped row.  The result
-// is the stable counting sort (experts ascending, flat index ascending inside an expert),
-// with no atomics, so it is the same on every run.
+// The flat assignments i = t*k + j are cut into chunks of 64, one wavefront each.  Inside a
+// chunk the lanes that hold the same local expert find each other with wavefront ballots,
+// so each assignment gets its rank among the earlier assignments of its expert in the chunk
+// and each (chunk, expert) its count, without atomics.  A scan per expert over the chunks
+// and a scan over the experts then give every (chunk, expert) its first grouped row, and a
+// last pass writes every assignment to base + rank.  The result is the stable counting sort
+// (experts ascending, flat index ascending inside an expert), identical on every run.
+//
+// Small batches (at most 16 chunks) run all three phases in one workgroup and one launch;
+// larger ones run a counting launch over all chunks, a one-workgroup scan, and a scatter
+// launch, so the ballot work spreads over the whole GPU.
 //
 // Row tiles: the grouped GEMMs are cut per expert from the real row count, not from the
 // token count ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
 // Selection", paragraphs 3-4): an expert with c rows gets ceil(c / tile_rows) tiles, rows
-// spread as evenly as 16-row steps allow.
+// spread as evenly as 16-row steps allow, so a hot expert of a concentrated routing gets
+// several tiles while a cold one gets one.
 #include "launch.hpp"
 
 namespace fmoe {
 
-constexpr int kGroupWaves = 8;
-constexpr int kGroupThreads = kGroupWaves * 64;
-constexpr int kGroupEPT = 2;  // experts per thread in phase 2 (local experts <= 1024)
+constexpr int kScanThreads = 1024;
+constexpr int kSmallChunks = 16;  // chunks (wavefronts) of the one-workgroup path
 
-// Exclusive scan of one int per thread over the workgroup; *total gets the sum.
-__device__ int block_exclusive_scan(int v, int* sh, int* total) {
+// Phase 1 for one chunk of 64 assignments, by one wavefront.  Writes the chunk's count of
+// every local expert to col[e * col_stride] (zeros included) and returns, for this lane, the
+// local expert (-1 when not local) and its rank inside the chunk; *bad gets the number of
+// ids outside [0, E) in the chunk (same value in every lane).  `mask` is per-wavefront LDS
+// scratch of El entries.
+__device__ void chunk_rank(const int32_t* __restrict__ ids, int n, int E, int El, int lo, int chunk, int* col,
+                           int col_stride, int* mask, int* out_l, int* out_r, int* bad) {
+    const int lane = lane_id();
+    for (int e = lane; e < El; e += 64) mask[e] = 0;
+    const int i = chunk * 64 + lane;
+    int l = -1, b = 0;
+    if (i < n) {
+        const int id = ids[i];
+        if (id < 0 || id >= E) b = 1;
+        else if (id - lo >= 0 && id - lo < El) l = id - lo;
+    }
+    *bad = __popcll(__ballot(b));
+    unsigned long long pending = __ballot(l >= 0);
+    int r = -1;
+    while (pending) {
+        const int leader = __ffsll((long long)pending) - 1;
+        const int lv = __shfl(l, leader, 64);
+        const unsigned long long m = __ballot(l == lv);
+        if (l == lv) r = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == leader) mask[lv] = __popcll(m);
+        pending &= ~m;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e = lane; e < El; e += 64) col[e * col_stride] = mask[e];
+    *out_l = l;
+    *out_r = r;
+}
+
+// Exclusive sum over the kScanThreads threads of the workgroup (thread order); *total gets
+// the sum.  sh: 32 ints of LDS.
+__device__ int block_scan_excl(int v, int* sh, int* total) {
     const int lane = lane_id(), wid = threadIdx.x >> 6;
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
+        const int y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
     }
     if (lane == 63) sh[wid] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int w = 0; w < kGroupWaves; w++) {
-            int c = sh[w];
-            sh[w] = run;
-            run += c;
+    if (wid == 0) {
+        int t = lane < kScanThreads / 64 ? sh[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(t, o, 64);
+            if (lane >= o) t += y;
         }
-        sh[kGroupWaves] = run;
+        if (lane < kScanThreads / 64) sh[16 + lane] = t;
     }
     __syncthreads();
-    int res = x - v + sh[wid];
-    *total = sh[kGroupWaves];
+    const int res = x - v + (wid > 0 ? sh[16 + wid - 1] : 0);
+    *total = sh[16 + kScanThreads / 64 - 1];
     __syncthreads();
     return res;
 }
@@ -56,159 +94,199 @@ __device__ int block_max(int v, int* sh) {
     if (lane == 0) sh[wid] = v;
     __syncthreads();
     int m = sh[0];
-    for (int w = 1; w < kGroupWaves; w++) m = max(m, sh[w]);
+    for (int q = 1; q < kScanThreads / 64; q++) m = max(m, sh[q]);
     __syncthreads();
     return m;
 }
 
-__global__ __launch_bounds__(kGroupThreads) void k_group(const int32_t* __restrict__ ids, int n, int E, int El,
-                                                        int lo, int tile_rows, int rows_estimate,
-                                                        int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
-                                                        int32_t* __restrict__ inv_perm, int32_t* __restrict__ rank_buf,
-                                                        MTile* __restrict__ mtiles, DevHeader* __restrict__ hdr) {
-    extern __shared__ int32_t lds[];
-    int* hist = lds;                          // [kGroupWaves][El]
-    int* sh = lds + kGroupWaves * El;         // scan scratch [kGroupWaves + 1]
-    long long* shl = (long long*)(sh + 16);   // dropped-id partial sums [kGroupWaves]
-    const int lane = lane_id(), wid = threadIdx.x >> 6;
-
-    for (int i = threadIdx.x; i < kGroupWaves * El; i += kGroupThreads) hist[i] = 0;
+// Phase 2 by one workgroup of kScanThreads: turns cnt[e * nchunk + c] (count of expert e in
+// chunk c) into the first grouped row of (e, c); writes counts, offsets, the row tiles and
+// the header.  Expert e's chunks are split over P = kScanThreads / El' threads (El' = El
+// rounded up to a power of two), threads in expert order.
+__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int rows_estimate, long long dropped,
+                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+                              DevHeader* __restrict__ hdr, int* sh /* >= kScanThreads + 32 ints */) {
+    int Ep = 1;
+    while (Ep < El) Ep <<= 1;
+    const int P = kScanThreads / Ep;  // threads per expert (>= 1 since El <= 1024)
+    const int e = threadIdx.x / P, part = threadIdx.x % P;
+    const bool live = e < El;
+    const int per = (nchunk + P - 1) / P;
+    const int c0 = min(nchunk, part * per), c1 = min(nchunk, c0 + per);
+    int s = 0;
+    if (live)
+        for (int c = c0; c < c1; c++) s += cnt[e * nchunk + c];
+    int* part_sum = sh + 32;  // [kScanThreads]
+    part_sum[threadIdx.x] = s;
     __syncthreads();
-
-    // ---- phase 1: in-segment ranks
-    const int seg = ((n + kGroupWaves * 64 - 1) / (kGroupWaves * 64)) * 64;
-    const int begin = wid * seg;
-    int* my_hist = hist + wid * El;
-    int bad = 0;
-    for (int c = 0; c < seg; c += 64) {
-        const int i = begin + c + lane;
-        int l = -1;
-        if (i < n) {
-            const int id = ids[i];
-            if (id < 0 || id >= E) bad++;
-            else if (id - lo >= 0 && id - lo < El) l = id - lo;
-        }
-        unsigned long long pending = __ballot(l >= 0);
-        int r = -1;
-        while (pending) {
-            const int leader = __ffsll((long long)pending) - 1;
-            const int lv = __shfl(l, leader, 64);
-            const unsigned long long m = __ballot(l == lv);
-            if (l == lv) r = my_hist[lv] + __popcll(m & ((1ull << lane) - 1ull));
-            if (lane == leader) my_hist[lv] += __popcll(m);
-            pending &= ~m;
-        }
-        if (i < n) rank_buf[i] = r;
+    int before = 0, total = 0;  // this part's prefix inside its expert, and the expert total
+    for (int q = 0; q < P; q++) {
+        const int v = part_sum[e * P + q];
+        if (q < part) before += v;
+        total += v;
     }
-    {
-        long long b = bad;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) b += __shfl_xor(b, o, 64);
-        if (lane == 0) shl[wid] = b;
+    const int lead = (live && part == 0);
+    int R, n_mtiles, empty;
+    const int first = block_scan_excl(lead ? total : 0, sh, &R);  // valid in the lead thread
+    const int ntile = lead ? (total + tile_rows - 1) / tile_rows : 0;
+    const int tfirst = block_scan_excl(ntile, sh, &n_mtiles);
+    (void)block_scan_excl(lead && total == 0, sh, &empty);
+    const int max_rows = block_max(lead ? total : 0, sh);
+    // hand the lead thread's expert offset and first tile to the other parts of the expert
+    int* e_first = part_sum;          // [Ep]
+    int* e_tfirst = part_sum + 512;   // [Ep] (Ep <= 1024 only when P == 1, then never read back)
+    if (P > 1) {
+        if (lead) {
+            e_first[e] = first;
+            e_tfirst[e] = tfirst;
+        }
+        __syncthreads();
     }
-    __syncthreads();
-
-    // ---- phase 2: per-expert scans, offsets, tiles
-    int cnt[kGroupEPT], run_total = 0;
-#pragma unroll
-    for (int q = 0; q < kGroupEPT; q++) {
-        const int e = threadIdx.x * kGroupEPT + q;
-        int run = 0;
-        if (e < El) {
-            for (int w = 0; w < kGroupWaves; w++) {
-                const int c = hist[w * El + e];
-                hist[w * El + e] = run;
-                run += c;
+    const int my_first = (P > 1) ? (live ? e_first[e] : 0) : first;
+    const int my_tfirst = (P > 1) ? (live ? e_tfirst[e] : 0) : tfirst;
+    if (live) {
+        int run = my_first + before;
+        for (int c = c0; c < c1; c++) {
+            const int v = cnt[e * nchunk + c];
+            cnt[e * nchunk + c] = run;
+            run += v;
+        }
+        if (part == 0) {
+            counts[e] = total;
+            offsets[e] = first;
+        }
+        // row tiles of expert e, split over its P threads
+        const int nt = (total + tile_rows - 1) / tile_rows;
+        if (nt > 0) {
+            const int per_tile = ((total + nt - 1) / nt + 15) / 16 * 16;  // even split, 16-row steps
+            for (int j = part; j < nt; j += P) {
+                MTile mt;
+                mt.expert = e;
+                mt.row0 = my_first + j * per_tile;
+                mt.rows = min(per_tile, total - j * per_tile);
+                mt.pad = 0;
+                mtiles[my_tfirst + j] = mt;
             }
-        }
-        cnt[q] = run;
-        run_total += run;
-    }
-    int R;
-    const int base = block_exclusive_scan(run_total, sh, &R);
-    int ntile[kGroupEPT], nt_total = 0, local_max = 0, local_empty = 0;
-    {
-        int off = base;
-#pragma unroll
-        for (int q = 0; q < kGroupEPT; q++) {
-            const int e = threadIdx.x * kGroupEPT + q;
-            ntile[q] = 0;
-            if (e < El) {
-                counts[e] = cnt[q];
-                offsets[e] = off;
-                for (int w = 0; w < kGroupWaves; w++) hist[w * El + e] += off;
-                ntile[q] = (cnt[q] + tile_rows - 1) / tile_rows;
-                local_max = max(local_max, cnt[q]);
-                local_empty += cnt[q] == 0;
-            }
-            off += cnt[q];
-            nt_total += ntile[q];
-        }
-    }
-    int n_mtiles;
-    const int tbase = block_exclusive_scan(nt_total, sh, &n_mtiles);
-    int empty_total;
-    (void)block_exclusive_scan(local_empty, sh, &empty_total);
-    const int max_rows = block_max(local_max, sh);
-    {
-        int tpos = tbase, off = base;
-#pragma unroll
-        for (int q = 0; q < kGroupEPT; q++) {
-            const int e = threadIdx.x * kGroupEPT + q;
-            if (e < El && ntile[q] > 0) {
-                // rows per tile: even split rounded up to 16, so every tile but the last is full
-                const int per = ((cnt[q] + ntile[q] - 1) / ntile[q] + 15) / 16 * 16;
-                for (int j = 0; j < ntile[q]; j++) {
-                    MTile mt;
-                    mt.expert = e;
-                    mt.row0 = off + j * per;
-                    mt.rows = min(per, cnt[q] - j * per);
-                    mt.pad = 0;
-                    mtiles[tpos + j] = mt;
-                }
-            }
-            tpos += ntile[q];
-            off += cnt[q];
         }
     }
     if (threadIdx.x == 0) {
         offsets[El] = R;
-        long long dropped = 0;
-        for (int w = 0; w < kGroupWaves; w++) dropped += shl[w];
         hdr->m_tiles = n_mtiles;
         hdr->local_rows = R;
         hdr->max_rows = max_rows;
-        hdr->empty_experts = empty_total;
+        hdr->empty_experts = empty;
         hdr->dropped = dropped;
         hdr->tile_rows = tile_rows;
         hdr->rows_estimate = rows_estimate;
     }
-    __syncthreads();
+}
 
-    // ---- phase 3: scatter
-    for (int c = 0; c < seg; c += 64) {
-        const int i = begin + c + lane;
-        if (i >= n) break;
-        const int id = ids[i];
-        const int l = id - lo;
-        if (id >= 0 && id < E && l >= 0 && l < El) {
-            const int pos = my_hist[l] + rank_buf[i];
-            perm_src[pos] = i;
-            inv_perm[i] = pos;
-        } else {
-            inv_perm[i] = -1;
-        }
+// Phase 3 for one assignment: it goes to base(expert, chunk) + rank.
+__device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int base, int32_t* __restrict__ perm_src,
+                                              int32_t* __restrict__ inv_perm) {
+    if (i >= n) return;
+    if (l >= 0) {
+        const int pos = base + r;
+        perm_src[pos] = i;
+        inv_perm[i] = pos;
+    } else {
+        inv_perm[i] = -1;
     }
 }
 
-size_t group_lds_bytes(int El) { return (size_t)(kGroupWaves * El + 16 + 2 * kGroupWaves) * sizeof(int32_t); }
+// ---------------------------------------------------------------- one-workgroup path
 
-hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int rows_estimate, int32_t* counts,
-                        int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf, MTile* mtiles,
-                        DevHeader* hdr, hipStream_t st) {
-    k_group<<<1, kGroupThreads, group_lds_bytes(El), st>>>(ids, n, E, El, lo, tile_rows, rows_estimate, counts, offsets, perm_src,
-                                                            inv_perm, rank_buf, mtiles, hdr);
+__global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
+                                                             int lo, int tile_rows, int rows_estimate,
+                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm_src,
+                                                             int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
+                                                             DevHeader* __restrict__ hdr) {
+    extern __shared__ int lds[];
+    const int nchunk = (n + 63) / 64;  // <= kSmallChunks
+    int* cnt = lds;                        // [El][nchunk]
+    int* mask = cnt + El * nchunk;         // [nchunk][El]
+    int* bads = mask + nchunk * El;        // [kSmallChunks]
+    int* sh = bads + kSmallChunks;         // scan scratch [kScanThreads + 32]
+    const int w = threadIdx.x >> 6;
+    int l = -1, r = -1, bad = 0;
+    if (w < nchunk) chunk_rank(ids, n, E, El, lo, w, cnt + w, nchunk, mask + w * El, &l, &r, &bad);
+    if (w < nchunk && lane_id() == 0) bads[w] = bad;
+    __syncthreads();
+    long long dropped = 0;
+    for (int c = 0; c < nchunk; c++) dropped += bads[c];
+    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, hdr, sh);
+    __syncthreads();
+    if (w < nchunk) chunk_scatter(w * 64 + lane_id(), n, l, r, l >= 0 ? cnt[l * nchunk + w] : 0, perm_src, inv_perm);
+}
+
+// ---------------------------------------------------------------- multi-workgroup path
+
+// One wavefront per chunk, 4 per workgroup: counts go to cnt[e * nchunk + chunk], ranks to
+// rank_buf, the chunk's ids outside [0,E) to bad_buf[chunk].
+__global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
+                                                     int nchunk, int* __restrict__ cnt, int32_t* __restrict__ rank_buf,
+                                                     int* __restrict__ bad_buf) {
+    extern __shared__ int lds[];
+    const int w = threadIdx.x >> 6;
+    const int chunk = blockIdx.x * 4 + w;
+    if (chunk >= nchunk) return;
+    int l, r, bad;
+    chunk_rank(ids, n, E, El, lo, chunk, cnt + chunk, nchunk, lds + w * El, &l, &r, &bad);
+    const int i = chunk * 64 + lane_id();
+    if (i < n) rank_buf[i] = r;
+    if (lane_id() == 0) bad_buf[chunk] = bad;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
+                                                            int rows_estimate, const int* __restrict__ bad_buf,
+                                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                            MTile* __restrict__ mtiles, DevHeader* __restrict__ hdr) {
+    __shared__ int sh[kScanThreads + 32];
+    __shared__ long long dsum[kScanThreads / 64];
+    long long d = 0;
+    for (int c = threadIdx.x; c < nchunk; c += kScanThreads) d += bad_buf[c];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+    if (lane_id() == 0) dsum[threadIdx.x >> 6] = d;
+    __syncthreads();
+    long long dropped = 0;
+    for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
+    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, hdr, sh);
+}
+
+__global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
+                                                       int nchunk, const int* __restrict__ cnt,
+                                                       const int32_t* __restrict__ rank_buf,
+                                                       int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int id = ids[i];
+    const int l = (id >= 0 && id < E && id - lo >= 0 && id - lo < El) ? id - lo : -1;
+    chunk_scatter(i, n, l, rank_buf[i], l >= 0 ? cnt[l * nchunk + i / 64] : 0, perm_src, inv_perm);
+}
+
+size_t group_scratch_bytes(long long n, int El) {
+    const long long nchunk = (n + 63) / 64;
+    return (size_t)(nchunk * El + nchunk) * sizeof(int);
+}
+
+hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int rows_estimate,
+                        int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
+                        int* scratch, MTile* mtiles, DevHeader* hdr, hipStream_t st) {
+    const int nchunk = (n + 63) / 64;
+    const size_t lds = (size_t)(2 * El * nchunk + kSmallChunks + kScanThreads + 32) * 4;
+    if (nchunk <= kSmallChunks && lds <= 65536) {
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, rows_estimate, counts, offsets,
+                                                    perm_src, inv_perm, mtiles, hdr);
+        return hipGetLastError();
+    }
+    int* cnt = scratch;                        // [El][nchunk]
+    int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
+    k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, rows_estimate, bad, counts, offsets, mtiles,
+                                             hdr);
+    k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);
     return hipGetLastError();
 }
 

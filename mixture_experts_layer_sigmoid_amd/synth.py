@@ -157,13 +157,17 @@ def block_quantize_fp8(w: torch.Tensor):
     E, N, K = w.shape
     codes = torch.empty((E, N, K), dtype=torch.uint8)
     scales = torch.empty((E, N // 128, K // 128), dtype=torch.float32)
-    for e in range(E):
+
+    def one(e):
         b = w[e].float().reshape(N // 128, 128, K // 128, 128)
         amax = b.abs().amax(dim=(1, 3))
         s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
         q = (b / s[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
         codes[e] = q.reshape(N, K).view(torch.uint8)
         scales[e] = s
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(one, range(E)))
     return codes, scales
 
 

@@ -42,7 +42,8 @@ def test_bf16_layer_small(T, H, I, E, k, routing, scoring):
     check_layer(L, n_sample=10 ** 6)
 
 
-@pytest.mark.parametrize("T,H,I,E,k,ep", [(50, 512, 256, 8, 2, 1), (40, 256, 384, 16, 6, 2), (200, 256, 256, 4, 2, 1)])
+@pytest.mark.parametrize("T,H,I,E,k,ep", [(50, 512, 256, 8, 2, 1), (40, 256, 384, 16, 6, 2), (200, 256, 256, 4, 2, 1),
+                                          (20, 128, 128, 4, 2, 1)])  # one 128-deep block: idle split-K waves
 def test_fp8_layer_small(T, H, I, E, k, ep):
     announce(f"fp8 layer T={T} H={H} I={I} E={E} k={k} ep={ep}")
     L = Layer(config=91, T=T, H=H, I=I, E=E, k=k, fp8=True, ep_size=ep, ep_rank=ep - 1)
