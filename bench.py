@@ -234,6 +234,26 @@ def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
                        f"OpenMP over tokens, {threads} threads on {platform.processor() or platform.machine()}")
 
 
+def sweep_workloads(B3, synth):
+    """The T sweep of the bf16 layer (uniform and concentrated), the FP8 w8a8 layer, and the FP8
+    expert-parallel shard; the headline workload is not repeated."""
+    work = []
+    for T in (1, 8, 32, 128, 256, 512, 1024, 4096):
+        for routing in ("uniform", "concentrated"):
+            if (T == 256 and routing == "uniform") or (T == 1 and routing == "concentrated"):
+                continue
+            work.append(Workload(f"bf16 H2048 I768 E128 top8, T={T}, {routing}", config=B3, T=T, H=2048, I=768,
+                                 E=128, k=8, routing=routing))
+    for T in (64, 128, 256):
+        work.append(Workload(f"fp8 w8a8 H2048 I768 E128 top8, T={T}, uniform", config=synth.FP8_LAYER,
+                             weight_config=B3, T=T, H=2048, I=768, E=128, k=8, fp8=True))
+    for routing in ("uniform", "concentrated"):
+        work.append(Workload(f"fp8 shard H7168 I2048 top6 of 400 (ep 8, 50 local), T=288, {routing}",
+                             config=synth.EP_SHARD, T=288, H=7168, I=2048, E=400, k=6, fp8=True, routing=routing,
+                             ep_size=8, ep_rank=0))
+    return work
+
+
 def host_cpu():
     try:
         with open("/proc/cpuinfo") as f:
@@ -253,6 +273,11 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-steps", type=int, default=12)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a plain 256 MiB device copy (torch elementwise kernel): the reference launch "
+                         "for scaling hardware byte counters")
+    ap.add_argument("--workload", default=None,
+                    help="run only the sweep workloads whose name contains this text (profiling); no headline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this layer runs on a single MI355X (no collectives); "
@@ -266,8 +291,22 @@ def main():
 
     fm.load_library()
     torch.cuda.init()
+    if args.calibrate:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.add(src, 0.0, out=dst)  # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
     B3 = synth.BF16_LAYER
     head = Workload("bf16 H2048 I768 E128 top8, T=256, uniform", config=B3, T=256, H=2048, I=768, E=128, k=8)
+    if args.workload is not None:
+        picked = [wl for wl in [head] + sweep_workloads(B3, synth) if args.workload in wl.name]
+        rows = []
+        for wl in picked:
+            print(f"[bench] workload: {wl.name}", file=sys.stderr, flush=True)
+            rows.append(summarize(wl, measure(wl, args.steps, args.warmup)))
+        print(json.dumps(dict(metric=METRIC, workloads=rows)))
+        return
     print(f"[bench] headline: {head.name}", file=sys.stderr, flush=True)
     # the gate/up GEMM streams two thirds of the touched weight bytes: the dominant kernel
     dom = "gemm1"
@@ -288,23 +327,7 @@ def main():
 
     sweep = [hs]
     if not args.no_sweep:
-        work = []
-        for T in (1, 8, 32, 128, 256, 512, 1024, 4096):
-            for routing in ("uniform", "concentrated"):
-                if T == 256 and routing == "uniform":
-                    continue
-                if T == 1 and routing == "concentrated":
-                    continue
-                work.append(Workload(f"bf16 H2048 I768 E128 top8, T={T}, {routing}", config=B3, T=T, H=2048, I=768,
-                                     E=128, k=8, routing=routing))
-        for T in (64, 128, 256):
-            work.append(Workload(f"fp8 w8a8 H2048 I768 E128 top8, T={T}, uniform", config=synth.FP8_LAYER,
-                                 weight_config=B3, T=T, H=2048, I=768, E=128, k=8, fp8=True))
-        for routing in ("uniform", "concentrated"):
-            work.append(Workload(f"fp8 shard H7168 I2048 top6 of 400 (ep 8, 50 local), T=288, {routing}",
-                                 config=synth.EP_SHARD, T=288, H=7168, I=2048, E=400, k=6, fp8=True, routing=routing,
-                                 ep_size=8, ep_rank=0))
-        for wl in work:
+        for wl in sweep_workloads(B3, synth):
             print(f"[bench] sweep: {wl.name}", file=sys.stderr, flush=True)
             sweep.append(summarize(wl, measure(wl, args.sweep_steps, 3)))
             print(f"[bench]   p50 {sweep[-1]['us_p50']} us, {sweep[-1]['hbm_TBps']} TB/s", file=sys.stderr, flush=True)
