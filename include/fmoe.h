@@ -85,9 +85,11 @@ typedef struct {
     int32_t local_rows;      /* R = rows of this rank's experts                              */
     int32_t max_rows;        /* largest per-expert row count                                */
     int32_t empty_experts;   /* local experts with no row                                   */
-    int32_t m_tiles;         /* row tiles of the grouped GEMMs                              */
+    int32_t m_tiles;         /* row tiles of the grouped GEMMs (light + heavy)              */
     int32_t rows_estimate;   /* host plan: max(1, ceil(T*top_k/E))                          */
-    int32_t tile_rows;       /* host plan: largest row tile of the grouped GEMMs            */
+    int32_t tile_rows;       /* host plan: largest light tile (one per expert with 1..tile_rows
+                                rows); heavier experts get tiles of at most 128 rows         */
+    int32_t heavy_tiles;     /* row tiles of experts with more than tile_rows rows           */
 } fmoe_stats;
 
 int fmoe_abi_version(void);

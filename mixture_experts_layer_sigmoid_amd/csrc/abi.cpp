@@ -4,10 +4,11 @@
 // Plan ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
 // Selection", paragraph 3): the workspace is laid out for the worst case first (every
 // assignment local, any imbalance); then the rows-per-expert estimate
-// max(1, ceil(T*top_k/E)) with E the total physical expert slots picks the largest row tile
-// of the grouped GEMMs (16, 32, 64 or 128 rows).  The grouping kernel cuts each expert's real
-// row count into tiles of at most that size on the device, so concentrated routing gets
-// more tiles on its hot experts without a host round trip.
+// max(1, ceil(T*top_k/E)) with E the total physical expert slots picks the largest light row
+// tile (16 or 32 rows).  The grouping kernel sorts each expert by its real row count on the
+// device: one light tile when it fits, heavy tiles of up to 128 rows otherwise (the hot
+// experts of a concentrated routing, every expert of a large batch), without a host round
+// trip.  Both GEMM kernels run; the one with an empty tile list exits at once.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -38,8 +39,9 @@ struct Plan {
     bool fp8;
     long long n;         // T*k assignments
     int rows_estimate;   // max(1, ceil(T*k/E))
-    int tile_rows;       // largest row tile: 16, 32, 64 or 128
-    int max_mtiles;      // bound on row tiles for any routing
+    int tile_rows;       // largest light row tile: 16 or 32 (heavier experts use heavy tiles)
+    int max_light;       // bounds on light and heavy row tiles for any routing
+    int max_heavy;
     int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
     Layout L;
 };
@@ -76,7 +78,7 @@ Plan make_plan(const fmoe_shape* s) {
     // in two; heavier experts get more tiles on the device.
     const double need = p.rows_estimate + 3.0 * std::sqrt((double)p.rows_estimate) + 1.0;
     int tr = 16;
-    while (tr < need && tr < 128) tr <<= 1;
+    while (tr < need && tr < kLightRows) tr <<= 1;
     // FP8 stages the tile's activation scales in LDS: keep them within 64 KB
     while (p.fp8 && tr > 16 && gemm_lds_bytes(true, p.H > p.I ? p.H : p.I, tr) > 65536) tr >>= 1;
     p.tile_rows = tr;
@@ -91,11 +93,13 @@ Plan make_plan(const fmoe_shape* s) {
     };
     p.wk1 = pick_wk(p.I);
     p.wk2 = pick_wk(p.H);
-    // sum over experts of ceil(c_e / tile_rows) <= ceil(n / tile_rows) + (experts with a row),
-    // and no tile is empty
-    long long bound = (p.n + tr - 1) / tr + (p.El < p.n ? p.El : p.n);
-    if (bound > p.n) bound = p.n;
-    p.max_mtiles = (int)(bound < 1 ? 1 : bound);
+    // light tiles: one per expert with 1..tile_rows rows; heavy tiles: ceil(c/128) per expert
+    // with c > tile_rows rows, at most n/128 + (n / (tile_rows + 1)) in all; no tile is empty
+    const long long nl = p.El < p.n ? p.El : p.n;
+    long long nh = p.n / kHeavyRows + (p.n / (tr + 1) < p.El ? p.n / (tr + 1) : p.El) + 1;
+    if (nh > p.n) nh = p.n;
+    p.max_light = (int)(nl < 1 ? 1 : nl);
+    p.max_heavy = (int)(nh < 1 ? 1 : nh);
 
     Layout& L = p.L;
     size_t o = 0;
@@ -114,7 +118,7 @@ Plan make_plan(const fmoe_shape* s) {
     L.inv = take(n * 4);
     L.rank = take(n * 4);
     L.grp = take(group_scratch_bytes((long long)n, p.El));
-    L.mtiles = take((size_t)p.max_mtiles * sizeof(MTile));
+    L.mtiles = take((size_t)(p.max_light + p.max_heavy) * sizeof(MTile));
     if (p.fp8) {
         L.xq = take((size_t)p.T * p.H);
         L.xs = take((size_t)p.T * (p.H / 128) * 4);
@@ -174,9 +178,12 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     const int cus = device_cus();
 
     record(ev, FMOE_STAGE_GROUP, st);
+    MTile* mtiles_heavy = mtiles + p.max_light;
     FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, (int32_t*)(ws + L.counts),
                           (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
-                          hdr, st));
+                          mtiles_heavy, hdr, st));
+    // an expert can hold more than tile_rows rows only if there are more assignments than that
+    const bool heavy_possible = p.n > p.tile_rows;
 
     record(ev, FMOE_STAGE_QUANT_X, st);
     if (p.fp8) FMOE_TRY(launch_quant_rows(x, true, p.T, p.H, (uint8_t*)(ws + L.xq), (float*)(ws + L.xs), nullptr, st));
@@ -195,8 +202,14 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g1.K = p.H;
     g1.out = ws + L.h;
     g1.mtiles = mtiles;
-    g1.hdr = hdr;
-    FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_mtiles, cus, st));
+    g1.tile_count = &hdr->m_tiles;
+    FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_light, cus, st));
+    if (heavy_possible) {
+        GemmArgs g1h = g1;
+        g1h.mtiles = mtiles_heavy;
+        g1h.tile_count = &hdr->m_tiles_heavy;
+        FMOE_TRY(launch_grouped_gemm_heavy(true, p.fp8, p.fp8, g1h, p.max_heavy, cus, st));
+    }
 
     record(ev, FMOE_STAGE_QUANT_H, st);
     if (p.fp8)
@@ -216,8 +229,14 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g2.K = p.I;
     g2.out = ws + L.y;
     g2.mtiles = mtiles;
-    g2.hdr = hdr;
-    FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.wk2, p.max_mtiles, cus, st));
+    g2.tile_count = &hdr->m_tiles;
+    FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.wk2, p.max_light, cus, st));
+    if (heavy_possible) {
+        GemmArgs g2h = g2;
+        g2h.mtiles = mtiles_heavy;
+        g2h.tile_count = &hdr->m_tiles_heavy;
+        FMOE_TRY(launch_grouped_gemm_heavy(false, p.fp8, false, g2h, p.max_heavy, cus, st));
+    }
 
     record(ev, FMOE_STAGE_COMBINE, st);
     FMOE_TRY(launch_combine(ws + L.y, inv, wts, p.T, p.k, p.H, out, st));
@@ -303,9 +322,10 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
     if (!aligned16(ws)) return FMOE_ERR_ARG;
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
     char* wsb = (char*)ws;
+    MTile* mt = (MTile*)(wsb + p.L.mtiles);
     return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, counts, offsets,
-                                   perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp),
-                                   (MTile*)(wsb + p.L.mtiles), (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
+                                   perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp), mt,
+                                   mt + p.max_light, (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
 }
 
 int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids, const float* topk_weights,
@@ -348,7 +368,8 @@ int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {
     out->local_rows = h.local_rows;
     out->max_rows = h.max_rows;
     out->empty_experts = h.empty_experts;
-    out->m_tiles = h.m_tiles;
+    out->m_tiles = h.m_tiles + h.m_tiles_heavy;
+    out->heavy_tiles = h.m_tiles_heavy;
     out->tile_rows = h.tile_rows;
     out->rows_estimate = h.rows_estimate;
     return FMOE_OK;

@@ -7,6 +7,9 @@
 // A rows are gathered: grouped row p reads activation row perm_src[p] / top_k (the gather
 // is fused into the operand load), or row p itself when no map is given.
 //
+// This light kernel takes row tiles of at most 32 rows (experts with few rows); heavier
+// experts go to gemm_heavy.hip.
+//
 // Shape of the work: weights are the bytes that matter (at decode every weight byte is used
 // by a handful of rows), so each wavefront streams its own 16 weight rows straight from HBM
 // into registers as the MFMA "A" operand (16 rows x 8 consecutive k per lane, 16-byte
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmArgs g) {
     const int w = uniform(threadIdx.x >> 6);
     const int wn = w % WN, wk = w / WN;
     const int nblocks = g.N / (16 * WN);
-    const int total = g.hdr->m_tiles * nblocks;
+    const int total = *g.tile_count * nblocks;
     const int nkb = g.K >> 7;
     float* wsc = dyn;             // FP8: [2][nkb] gate/up weight-block scales of the tile
     float* asc = dyn + 2 * nkb;   // FP8: [16*BMS][nkb] activation scales of the tile rows
@@ -324,8 +327,6 @@ static hipError_t launch_kind(const GemmArgs& a, int tile_rows, int wk, int max_
     switch (tile_rows) {
         case 16: return launch_bms<GATED, FP8, OUT_F32, 1>(a, wk, max_tiles, cus, st);
         case 32: return launch_bms<GATED, FP8, OUT_F32, 2>(a, wk, max_tiles, cus, st);
-        case 64: return launch_bms<GATED, FP8, OUT_F32, 4>(a, wk, max_tiles, cus, st);
-        case 128: return launch_bms<GATED, FP8, OUT_F32, 8>(a, wk, max_tiles, cus, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -15,15 +15,17 @@
 //
 // Row tiles: the grouped GEMMs are cut per expert from the real row count, not from the
 // token count ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
-// Selection", paragraphs 3-4): an expert with c rows gets ceil(c / tile_rows) tiles, rows
-// spread as evenly as 16-row steps allow, so a hot expert of a concentrated routing gets
-// several tiles while a cold one gets one.
+// Selection", paragraphs 3-4): an expert with 1..tile_rows rows becomes one tile of the light
+// GEMM kernel, a heavier one (a hot expert of a concentrated routing, or any expert of a large
+// batch) is cut into tiles of at most 128 rows for the heavy kernel, rows spread as evenly as
+// 16-row steps allow.
 #include "launch.hpp"
 
 namespace fmoe {
 
 constexpr int kScanThreads = 1024;
 constexpr int kSmallChunks = 16;  // chunks (wavefronts) of the one-workgroup path
+constexpr int kScanShared = 32 + 1536;  // LDS ints of scan_and_tile
 
 // Phase 1 for one chunk of 64 assignments, by one wavefront.  Writes the chunk's count of
 // every local expert to col[e * col_stride] (zeros included) and returns, for this lane, the
@@ -99,79 +101,116 @@ __device__ int block_max(int v, int* sh) {
     return m;
 }
 
-// Phase 2 by one workgroup of kScanThreads: turns cnt[e * nchunk + c] (count of expert e in
+// Phase 2 by one workgroup of kScanThreads: turns cnt[c * El + e] (count of expert e in
 // chunk c) into the first grouped row of (e, c); writes counts, offsets, the row tiles and
-// the header.  Expert e's chunks are split over P = kScanThreads / El' threads (El' = El
-// rounded up to a power of two), threads in expert order.
+// the header.  Thread t works on expert e = t % El' and part p = t / El' of its chunks
+// (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
+// threads read consecutive experts of a chunk.
 __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int rows_estimate, long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
-                              DevHeader* __restrict__ hdr, int* sh /* >= kScanThreads + 32 ints */) {
+                              MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
+                              int* sh /* >= kScanShared ints */) {
     int Ep = 1;
     while (Ep < El) Ep <<= 1;
-    const int P = kScanThreads / Ep;  // threads per expert (>= 1 since El <= 1024)
-    const int e = threadIdx.x / P, part = threadIdx.x % P;
+    const int P = kScanThreads / Ep;  // parts per expert (>= 1 since El <= 1024)
+    const int e = threadIdx.x % Ep, part = threadIdx.x / Ep;
     const bool live = e < El;
     const int per = (nchunk + P - 1) / P;
     const int c0 = min(nchunk, part * per), c1 = min(nchunk, c0 + per);
     int s = 0;
-    if (live)
-        for (int c = c0; c < c1; c++) s += cnt[e * nchunk + c];
-    int* part_sum = sh + 32;  // [kScanThreads]
+    if (live) {
+        int c = c0;
+        for (; c + 8 <= c1; c += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = cnt[(c + j) * El + e];
+#pragma unroll
+            for (int j = 0; j < 8; j++) s += v[j];
+        }
+        for (; c < c1; c++) s += cnt[c * El + e];
+    }
+    int* part_sum = sh + 32;  // [kScanThreads], later 3 x [512]
     part_sum[threadIdx.x] = s;
     __syncthreads();
     int before = 0, total = 0;  // this part's prefix inside its expert, and the expert total
     for (int q = 0; q < P; q++) {
-        const int v = part_sum[e * P + q];
+        const int v = part_sum[q * Ep + e];
         if (q < part) before += v;
         total += v;
     }
     const int lead = (live && part == 0);
-    int R, n_mtiles, empty;
+    // an expert with 1..tile_rows rows is one light tile; a heavier one is cut into heavy
+    // tiles of at most kHeavyRows rows
+    const bool heavy = total > tile_rows;
+    const int nheavy = heavy ? (total + kHeavyRows - 1) / kHeavyRows : 0;
+    int R, n_light, n_heavy, empty;
     const int first = block_scan_excl(lead ? total : 0, sh, &R);  // valid in the lead thread
-    const int ntile = lead ? (total + tile_rows - 1) / tile_rows : 0;
-    const int tfirst = block_scan_excl(ntile, sh, &n_mtiles);
+    const int lfirst = block_scan_excl(lead && total > 0 && !heavy, sh, &n_light);
+    const int hfirst = block_scan_excl(lead ? nheavy : 0, sh, &n_heavy);
     (void)block_scan_excl(lead && total == 0, sh, &empty);
     const int max_rows = block_max(lead ? total : 0, sh);
-    // hand the lead thread's expert offset and first tile to the other parts of the expert
-    int* e_first = part_sum;          // [Ep]
-    int* e_tfirst = part_sum + 512;   // [Ep] (Ep <= 1024 only when P == 1, then never read back)
+    // hand the lead thread's expert offset and first tiles to the other parts of the expert
+    int* e_first = part_sum;           // [Ep]  (P > 1 means Ep <= 512; with P == 1 these are
+    int* e_lfirst = part_sum + 512;    // [Ep]   never written)
+    int* e_hfirst = part_sum + 1024;   // [Ep]
     if (P > 1) {
         if (lead) {
             e_first[e] = first;
-            e_tfirst[e] = tfirst;
+            e_lfirst[e] = lfirst;
+            e_hfirst[e] = hfirst;
         }
         __syncthreads();
     }
     const int my_first = (P > 1) ? (live ? e_first[e] : 0) : first;
-    const int my_tfirst = (P > 1) ? (live ? e_tfirst[e] : 0) : tfirst;
+    const int my_lfirst = (P > 1) ? (live ? e_lfirst[e] : 0) : lfirst;
+    const int my_hfirst = (P > 1) ? (live ? e_hfirst[e] : 0) : hfirst;
     if (live) {
         int run = my_first + before;
-        for (int c = c0; c < c1; c++) {
-            const int v = cnt[e * nchunk + c];
-            cnt[e * nchunk + c] = run;
+        int c = c0;
+        for (; c + 8 <= c1; c += 8) {
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = cnt[(c + j) * El + e];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                cnt[(c + j) * El + e] = run;
+                run += v[j];
+            }
+        }
+        for (; c < c1; c++) {
+            const int v = cnt[c * El + e];
+            cnt[c * El + e] = run;
             run += v;
         }
         if (part == 0) {
             counts[e] = total;
             offsets[e] = first;
         }
-        // row tiles of expert e, split over its P threads
-        const int nt = (total + tile_rows - 1) / tile_rows;
-        if (nt > 0) {
-            const int per_tile = ((total + nt - 1) / nt + 15) / 16 * 16;  // even split, 16-row steps
-            for (int j = part; j < nt; j += P) {
+        // row tiles of expert e (heavy ones split over its P threads)
+        if (total > 0 && !heavy && part == 0) {
+            MTile mt;
+            mt.expert = e;
+            mt.row0 = my_first;
+            mt.rows = total;
+            mt.pad = 0;
+            mtiles[my_lfirst] = mt;
+        }
+        if (heavy) {
+            const int per_tile = ((total + nheavy - 1) / nheavy + 15) / 16 * 16;  // even split, 16-row steps
+            for (int j = part; j < nheavy; j += P) {
                 MTile mt;
                 mt.expert = e;
                 mt.row0 = my_first + j * per_tile;
                 mt.rows = min(per_tile, total - j * per_tile);
                 mt.pad = 0;
-                mtiles[my_tfirst + j] = mt;
+                mtiles_heavy[my_hfirst + j] = mt;
             }
         }
     }
     if (threadIdx.x == 0) {
         offsets[El] = R;
-        hdr->m_tiles = n_mtiles;
+        hdr->m_tiles = n_light;
+        hdr->m_tiles_heavy = n_heavy;
         hdr->local_rows = R;
         hdr->max_rows = max_rows;
         hdr->empty_experts = empty;
@@ -201,28 +240,29 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
                                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
                                                              int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
+                                                             MTile* __restrict__ mtiles_heavy,
                                                              DevHeader* __restrict__ hdr) {
     extern __shared__ int lds[];
     const int nchunk = (n + 63) / 64;  // <= kSmallChunks
-    int* cnt = lds;                        // [El][nchunk]
+    int* cnt = lds;                        // [nchunk][El]
     int* mask = cnt + El * nchunk;         // [nchunk][El]
     int* bads = mask + nchunk * El;        // [kSmallChunks]
-    int* sh = bads + kSmallChunks;         // scan scratch [kScanThreads + 32]
+    int* sh = bads + kSmallChunks;         // scan scratch [kScanShared]
     const int w = threadIdx.x >> 6;
     int l = -1, r = -1, bad = 0;
-    if (w < nchunk) chunk_rank(ids, n, E, El, lo, w, cnt + w, nchunk, mask + w * El, &l, &r, &bad);
+    if (w < nchunk) chunk_rank(ids, n, E, El, lo, w, cnt + w * El, 1, mask + w * El, &l, &r, &bad);
     if (w < nchunk && lane_id() == 0) bads[w] = bad;
     __syncthreads();
     long long dropped = 0;
     for (int c = 0; c < nchunk; c++) dropped += bads[c];
-    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
     __syncthreads();
-    if (w < nchunk) chunk_scatter(w * 64 + lane_id(), n, l, r, l >= 0 ? cnt[l * nchunk + w] : 0, perm_src, inv_perm);
+    if (w < nchunk) chunk_scatter(w * 64 + lane_id(), n, l, r, l >= 0 ? cnt[w * El + l] : 0, perm_src, inv_perm);
 }
 
 // ---------------------------------------------------------------- multi-workgroup path
 
-// One wavefront per chunk, 4 per workgroup: counts go to cnt[e * nchunk + chunk], ranks to
+// One wavefront per chunk, 4 per workgroup: counts go to cnt[chunk * El + e], ranks to
 // rank_buf, the chunk's ids outside [0,E) to bad_buf[chunk].
 __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
                                                      int nchunk, int* __restrict__ cnt, int32_t* __restrict__ rank_buf,
@@ -232,7 +272,7 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
     const int chunk = blockIdx.x * 4 + w;
     if (chunk >= nchunk) return;
     int l, r, bad;
-    chunk_rank(ids, n, E, El, lo, chunk, cnt + chunk, nchunk, lds + w * El, &l, &r, &bad);
+    chunk_rank(ids, n, E, El, lo, chunk, cnt + (size_t)chunk * El, 1, lds + w * El, &l, &r, &bad);
     const int i = chunk * 64 + lane_id();
     if (i < n) rank_buf[i] = r;
     if (lane_id() == 0) bad_buf[chunk] = bad;
@@ -241,8 +281,9 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
                                                             int rows_estimate, const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                            MTile* __restrict__ mtiles, DevHeader* __restrict__ hdr) {
-    __shared__ int sh[kScanThreads + 32];
+                                                            MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
+                                                            DevHeader* __restrict__ hdr) {
+    __shared__ int sh[kScanShared];
     __shared__ long long dsum[kScanThreads / 64];
     long long d = 0;
     for (int c = threadIdx.x; c < nchunk; c += kScanThreads) d += bad_buf[c];
@@ -252,7 +293,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
 }
 
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
@@ -263,7 +304,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
     if (i >= n) return;
     const int id = ids[i];
     const int l = (id >= 0 && id < E && id - lo >= 0 && id - lo < El) ? id - lo : -1;
-    chunk_scatter(i, n, l, rank_buf[i], l >= 0 ? cnt[l * nchunk + i / 64] : 0, perm_src, inv_perm);
+    chunk_scatter(i, n, l, rank_buf[i], l >= 0 ? cnt[(size_t)(i / 64) * El + l] : 0, perm_src, inv_perm);
 }
 
 size_t group_scratch_bytes(long long n, int El) {
@@ -273,19 +314,19 @@ size_t group_scratch_bytes(long long n, int El) {
 
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
-                        int* scratch, MTile* mtiles, DevHeader* hdr, hipStream_t st) {
+                        int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
-    const size_t lds = (size_t)(2 * El * nchunk + kSmallChunks + kScanThreads + 32) * 4;
+    const size_t lds = (size_t)(2 * El * nchunk + kSmallChunks + kScanShared) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
         k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, rows_estimate, counts, offsets,
-                                                    perm_src, inv_perm, mtiles, hdr);
+                                                    perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
         return hipGetLastError();
     }
-    int* cnt = scratch;                        // [El][nchunk]
+    int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
     k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, rows_estimate, bad, counts, offsets, mtiles,
-                                             hdr);
+                                             mtiles_heavy, hdr);
     k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);
     return hipGetLastError();
 }

@@ -16,8 +16,8 @@ struct GemmArgs {
     const float* S1;
     int N, K;
     void* out;                // [R, N] bf16, or fp32
-    const MTile* mtiles;
-    const DevHeader* hdr;
+    const MTile* mtiles;      // this kernel's row-tile list
+    const int* tile_count;    // its length (written by the grouping kernel)
 };
 
 hipError_t launch_router_logits(const void* x, const void* w, int T, int H, int E, float* logits, hipStream_t st);
@@ -26,12 +26,14 @@ hipError_t launch_router_topk(const void* logits, bool bf16, int T, int E, int k
 size_t group_scratch_bytes(long long n, int El);
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
-                        int* scratch, MTile* mtiles, DevHeader* hdr, hipStream_t st);
+                        int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int cols, uint8_t* q, float* s,
                              const DevHeader* rows_hdr, hipStream_t st);
 size_t gemm_lds_bytes(bool fp8, int K, int tile_rows);
 hipError_t launch_grouped_gemm(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows, int wk,
                                int max_tiles, int cus, hipStream_t st);
+hipError_t launch_grouped_gemm_heavy(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,
+                                     hipStream_t st);
 hipError_t launch_combine(const void* Y, const int32_t* inv_perm, const float* w, int T, int k, int H, void* out,
                           hipStream_t st);
 
