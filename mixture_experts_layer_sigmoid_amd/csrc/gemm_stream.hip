@@ -1,0 +1,341 @@
+// gemm_stream.hip -- grouped expert GEMMs for light row tiles (up to 32 rows), streaming form.
+//
+// Same operation as gemm.hip (gate/up with SiLU-and-mul, or down; bf16 or FP8 block-scaled),
+// for launches with enough tasks (row tile x 64 output features) to fill the GPU without
+// splitting the reduction.
+//
+// Decode is bound by the weight stream, so each wavefront is built as one uninterrupted
+// stream of weight loads: it walks its workgroup's tasks in order and its ring of D weight
+// steps (HBM straight into the MFMA "A" registers, 16 feature rows x 8 consecutive k per lane)
+// runs up to D steps ahead across task boundaries, so the stream never drains between tiles.
+// The tile's activation rows (the MFMA "B" operand) are the same for the 4 wavefronts of the
+// workgroup: they are loaded once per workgroup, a chunk of CS reduction steps at a time,
+// through registers into a double-buffered LDS area (each 64-lane fragment is stored in the
+// lane order the MFMA reads it, so stores and reads are contiguous 16-byte accesses), with the
+// next chunk in flight while the current one is used.  Loading them per wavefront instead
+// quadruples the vector-memory instructions of the activations, which then hold back the
+// weight stream.  FP8 scales of a chunk (one per 128-deep block and row, and one per
+// 128-deep block of the weight rows) are staged with it.
+//
+// Every step issues the same loads (padding steps past the reduction end re-read the last
+// valid step, which hits in cache), so the compiler's static wait counts stay exact.
+#include "launch.hpp"
+
+namespace fmoe {
+
+namespace {
+
+constexpr int kStreamFeatures = 64;  // output features per workgroup (4 wavefronts x 16)
+
+template <bool FP8>
+struct SCfg {
+    using T = bf16x8;
+    static constexpr int KSTEP = 32;   // reduction depth of one MFMA
+    static constexpr int EB = 2;       // bytes per element
+    static constexpr int LANE_B = 16;  // operand bytes per lane per step
+    static constexpr int HALVES = 1;   // 16-byte pieces per lane fragment
+    static constexpr int CS = 8;       // steps per staged chunk
+};
+template <>
+struct SCfg<true> {
+    using T = i32x8;
+    static constexpr int KSTEP = 128;
+    static constexpr int EB = 1;
+    static constexpr int LANE_B = 32;
+    static constexpr int HALVES = 2;
+    static constexpr int CS = 4;
+};
+
+template <bool FP8, int NS>
+struct StreamLds {
+    static constexpr int F = NS * SCfg<FP8>::CS * SCfg<FP8>::HALVES;  // 1 KB pieces per chunk
+    i32x4 x[2][F][64];
+    float asc[2][SCfg<FP8>::CS][NS * 16];  // FP8: activation scale of each step and tile row
+    float wsc[2][2][SCfg<FP8>::CS];        // FP8: weight-block scale of each matrix and step
+};
+
+__device__ __forceinline__ float silu_mul_s(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// a[i] for a lane-dependent i, as selects (an indexed read of a register array would go
+// through scratch memory)
+template <int N, typename T>
+__device__ __forceinline__ T pick(const T (&a)[N], int i) {
+    T r = a[0];
+#pragma unroll
+    for (int j = 1; j < N; j++) r = i == j ? a[j] : r;
+    return r;
+}
+
+// Where one task's operands live, for this lane.
+template <int NS, int NW>
+struct Ctx {
+    const uint8_t* w[NW];  // weight rows of this wavefront's 16 features, at this lane's (row, k) slot
+    const float* ws[NW];   // FP8: this workgroup's weight-block scale row ([K/128])
+    int map[NS];           // gather-map entry of this lane's row in each 16-row sub-block (its
+                           // activation row is map / top_k); read only when the task's
+                           // activations are staged, well after the load was issued
+    int row0, rows;        // grouped rows of the task
+    int soff;              // 0, or the step count for a padding context that re-reads the last step
+};
+
+template <bool GATED, bool FP8, bool OUT_F32, int NS, int D>
+__global__ __launch_bounds__(256) void k_grouped_gemm_stream(GemmArgs g) {
+    using C = SCfg<FP8>;
+    using FT = typename C::T;
+    constexpr int NW = GATED ? 2 : 1;
+    constexpr int CS = C::CS;
+    constexpr int F = StreamLds<FP8, NS>::F;
+    constexpr int FPW = F / 4;  // pieces staged per wavefront
+    static_assert(F % 4 == 0 && CS % D == 0, "chunk shape");
+    __shared__ StreamLds<FP8, NS> L;
+
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int K = g.K;
+    const int nsteps = K / C::KSTEP;
+    const int nch = (nsteps + CS - 1) / CS;
+    const int nkb = K >> 7;
+    const int nblocks = g.N / kStreamFeatures;
+    const int total = *g.tile_count * nblocks;
+    if ((int)blockIdx.x >= total) return;
+    const int ntasks = (total - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+    const size_t rowbytes = (size_t)K * C::EB;
+    const size_t lane_w = (size_t)r16 * rowbytes + kg * C::LANE_B;
+
+    using CT = Ctx<NS, NW>;
+    // task i of this workgroup into slot c; past the last task, a padding context that keeps
+    // re-reading the last step of task `prev` (whose addresses are computed, not loaded, so
+    // nothing waits on an outstanding load) with activation row 0
+    auto load_ctx = [&](CT& c, int i, const CT& prev) {
+        if (i >= ntasks) {
+#pragma unroll
+            for (int h = 0; h < NW; h++) {
+                c.w[h] = prev.w[h];
+                c.ws[h] = prev.ws[h];
+            }
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++) c.map[sb] = 0;
+            c.row0 = prev.row0;
+            c.rows = prev.rows;
+            c.soff = nsteps;
+            return;
+        }
+        const int t = (int)blockIdx.x + i * (int)gridDim.x;
+        const int mt = t / nblocks;
+        const int nb = t - mt * nblocks;
+        // the tile list is read-only here: read it through the constant address space, so the
+        // (wavefront-uniform) read is a scalar load that does not wait on the weight stream
+        const i32x4 mv = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + mt);
+        const MTile m = {mv[0], mv[1], mv[2], mv[3]};
+        const size_t wrow = (size_t)m.expert * g.N + nb * kStreamFeatures + w * 16;
+        c.w[0] = (const uint8_t*)g.W0 + wrow * rowbytes + lane_w;
+        if constexpr (GATED) c.w[NW - 1] = (const uint8_t*)g.W1 + wrow * rowbytes + lane_w;
+        if constexpr (FP8) {
+            const size_t srow = ((size_t)m.expert * (g.N >> 7) + ((nb * kStreamFeatures) >> 7)) * nkb;
+            c.ws[0] = g.S0 + srow;
+            if constexpr (GATED) c.ws[NW - 1] = g.S1 + srow;
+        }
+#pragma unroll
+        for (int sb = 0; sb < NS; sb++) {
+            const int p = m.row0 + min(sb * 16 + r16, m.rows - 1);
+            c.map[sb] = g.perm_src ? g.perm_src[p] : p;
+        }
+        c.row0 = m.row0;
+        c.rows = m.rows;
+        c.soff = 0;
+    };
+
+    FT bw[D][NW];
+    auto issue_w = [&](int slot, const CT& c, int step) {
+        const size_t o = (size_t)min(step + c.soff, nsteps - 1) * (C::KSTEP * C::EB);
+#pragma unroll
+        for (int h = 0; h < NW; h++) bw[slot][h] = *(const FT*)(c.w[h] + o);
+    };
+
+    // staging of one chunk: wavefront w loads pieces w*FPW .. w*FPW+FPW-1; piece f is step
+    // f / (NS*HALVES), sub-block (f / HALVES) % NS, 16-byte half f % HALVES
+    i32x4 xst[FPW];
+    float ast = 0.f, wst = 0.f;
+    const int topk = g.perm_src ? g.topk : 1;
+    auto src_row = [&](const CT& c, int sb) { return c.map[sb] / topk; };
+    auto stage_load = [&](const CT& c, int chunk) {
+        size_t xoff[NS];
+#pragma unroll
+        for (int sb = 0; sb < NS; sb++) xoff[sb] = (size_t)src_row(c, sb) * rowbytes + kg * C::LANE_B;
+#pragma unroll
+        for (int j = 0; j < FPW; j++) {
+            const int f = w * FPW + j;
+            const int s = f / (NS * C::HALVES), sb = (f / C::HALVES) % NS, half = f % C::HALVES;
+            const size_t step = (size_t)min(chunk * CS + s + c.soff, nsteps - 1);
+            xst[j] = *(const i32x4*)((const uint8_t*)g.A + xoff[sb] + step * (C::KSTEP * C::EB) + half * 16);
+        }
+        if constexpr (FP8) {
+            // activation scales: thread t < CS*NS*16 takes step t / (NS*16) of row t % (NS*16),
+            // which is this lane's row (r16) of sub-block (lane / 16) % NS
+            const int t = threadIdx.x % (CS * NS * 16);
+            const int s = t / (NS * 16);
+            const int kb = min(chunk * CS + s + c.soff, nkb - 1);
+            ast = g.A_scale[(size_t)(pick(c.map, (lane >> 4) % NS) / topk) * nkb + kb];
+            // weight scales: thread t < NW*CS takes matrix t / CS, step t % CS
+            const int u = threadIdx.x % (NW * CS);
+            const int kw = min(chunk * CS + u % CS + c.soff, nkb - 1);
+            wst = pick(c.ws, u / CS)[kw];
+        }
+    };
+    auto stage_store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < FPW; j++) L.x[buf][w * FPW + j][lane] = xst[j];
+        if constexpr (FP8) {
+            const int t = threadIdx.x;
+            if (t < CS * NS * 16) L.asc[buf][t / (NS * 16)][t % (NS * 16)] = ast;
+            if (t < NW * CS) L.wsc[buf][t / CS][t % CS] = wst;
+        }
+    };
+
+    f32x4 acc[NS][NW];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int sb = 0; sb < NS; sb++)
+#pragma unroll
+            for (int h = 0; h < NW; h++) acc[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto compute = [&](int slot, int buf, int s) {
+#pragma unroll
+        for (int sb = 0; sb < NS; sb++) {
+            FT xb;
+            if constexpr (FP8) {
+                const i32x4 lo = L.x[buf][(s * NS + sb) * 2][lane];
+                const i32x4 hi = L.x[buf][(s * NS + sb) * 2 + 1][lane];
+                xb = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const float sa = L.asc[buf][s][sb * 16 + r16];
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int h = 0; h < NW; h++) {
+                    const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[slot][h], xb, zero, 0, 0, 0,
+                                                                                      0, 0, 0);
+                    const float cs = L.wsc[buf][h][s] * sa;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc[sb][h][i] = __builtin_fmaf(p[i], cs, acc[sb][h][i]);
+                }
+            } else {
+                xb = __builtin_bit_cast(bf16x8, L.x[buf][s * NS + sb][lane]);
+#pragma unroll
+                for (int h = 0; h < NW; h++)
+                    acc[sb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[slot][h], xb, acc[sb][h], 0, 0, 0);
+            }
+        }
+    };
+    // lane holds token column sb*16 + r16 and features n0 + 4*kg + i
+    auto epilogue = [&](const CT& c, int n0) {
+#pragma unroll
+        for (int sb = 0; sb < NS; sb++) {
+            const int col = sb * 16 + r16;
+            if (col >= c.rows) continue;
+            const size_t o = (size_t)(c.row0 + col) * g.N + n0 + kg * 4;
+            float r[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_s(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
+            if (OUT_F32) {
+                *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
+            } else {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+                *(uint2*)((uint16_t*)g.out + o) = pk;
+            }
+        }
+    };
+    auto task_n0 = [&](int i) {
+        const int t = (int)blockIdx.x + i * (int)gridDim.x;
+        return (t % nblocks) * kStreamFeatures + w * 16;
+    };
+
+    // Two context slots, used alternately (task i runs from slot i % 2 and reads ahead into
+    // the other), so no loaded value is ever copied between registers.
+    CT ca, cb;
+    load_ctx(ca, 0, ca);
+    load_ctx(cb, 1, ca);
+#pragma unroll
+    for (int d = 0; d < D; d++) issue_w(d, ca, d);
+    stage_load(ca, 0);
+    stage_store(0);
+    __syncthreads();
+    if (nch > 1) stage_load(ca, 1);
+    else stage_load(cb, 0);
+    zero_acc();
+
+    int buf = 0;
+    auto run_task = [&](int i, CT& cur, CT& nxt) {
+        for (int c = 0; c < nch; c++) {
+            const bool last = c == nch - 1;
+#pragma unroll
+            for (int s = 0; s < CS; s++) {
+                if (c * CS + s < nsteps) compute(s % D, buf, s);
+                if (!last || s + D < CS) issue_w(s % D, cur, c * CS + s + D);
+                else issue_w(s % D, nxt, s + D - CS);
+            }
+            // publish the staged chunk (the next one of this task, or the first of the next
+            // task) and start loading the one after it
+            stage_store(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+            if (last) {
+                epilogue(cur, task_n0(i));
+                zero_acc();
+                load_ctx(cur, i + 2, nxt);  // this slot now holds the task after the next
+                if (nch > 1) stage_load(nxt, 1);
+                else stage_load(cur, 0);
+            } else if (c + 2 < nch) {
+                stage_load(cur, c + 2);
+            } else {
+                stage_load(nxt, 0);
+            }
+        }
+    };
+    for (int i = 0; i < ntasks; i += 2) {
+        run_task(i, ca, cb);
+        if (i + 1 < ntasks) run_task(i + 1, cb, ca);
+    }
+}
+
+template <bool GATED, bool FP8, bool OUT_F32, int NS>
+hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
+    constexpr int D = FP8 ? 4 : 8;
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D>, 256,
+                                                          0) != hipSuccess || nb < 1)
+            nb = 1;
+        per_cu = nb;
+    }
+    long long grid = (long long)max_tiles * (a.N / kStreamFeatures);
+    const long long cap = (long long)cus * per_cu;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D><<<(unsigned)grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+template <bool GATED, bool FP8, bool OUT_F32>
+hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, int cus, hipStream_t st) {
+    if (tile_rows == 16) return launch_stream<GATED, FP8, OUT_F32, 1>(a, max_tiles, cus, st);
+    if (tile_rows == 32) return launch_stream<GATED, FP8, OUT_F32, 2>(a, max_tiles, cus, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows,
+                                      int max_tiles, int cus, hipStream_t st) {
+    if (gated) {
+        if (fp8) return out_f32 ? launch_stream_rows<true, true, true>(a, tile_rows, max_tiles, cus, st)
+                                : launch_stream_rows<true, true, false>(a, tile_rows, max_tiles, cus, st);
+        return launch_stream_rows<true, false, false>(a, tile_rows, max_tiles, cus, st);
+    }
+    if (fp8) return launch_stream_rows<false, true, false>(a, tile_rows, max_tiles, cus, st);
+    return launch_stream_rows<false, false, false>(a, tile_rows, max_tiles, cus, st);
+}
+
+}  // namespace fmoe

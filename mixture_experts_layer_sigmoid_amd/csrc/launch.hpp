@@ -32,6 +32,8 @@ hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int co
 size_t gemm_lds_bytes(bool fp8, int K, int tile_rows);
 hipError_t launch_grouped_gemm(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows, int wk,
                                int max_tiles, int cus, hipStream_t st);
+hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows,
+                                      int max_tiles, int cus, hipStream_t st);
 hipError_t launch_grouped_gemm_heavy(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,
                                      hipStream_t st);
 hipError_t launch_combine(const void* Y, const int32_t* inv_perm, const float* w, int T, int k, int H, void* out,

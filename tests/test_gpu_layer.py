@@ -50,6 +50,22 @@ def test_fp8_layer_small(T, H, I, E, k, ep):
     check_layer(L, n_sample=10 ** 6)
 
 
+# Shapes whose plans run the streaming light kernel (no split reduction) for GEMM1 and/or GEMM2,
+# covering 16- and 32-row tiles, single-chunk reductions, chunks padded past the reduction end
+# (bf16 chunks of 8 steps, FP8 of 4) and an expert-parallel shard.
+@pytest.mark.parametrize("T,H,I,E,k,ep,fp8", [
+    (64, 256, 512, 64, 8, 1, False),    # GEMM1 streamed, one chunk, 32-row tiles
+    (40, 1024, 384, 64, 4, 1, False),   # GEMM2 streamed, 12 steps in 2 chunks, 16-row tiles
+    (128, 1024, 1024, 64, 8, 1, True),  # FP8, both streamed
+    (64, 384, 640, 64, 8, 1, True),     # FP8 GEMM1 with 3 steps in a 4-step chunk
+    (96, 640, 256, 128, 8, 2, True),    # FP8 GEMM2 with 2 steps in a chunk, rank 1 of 2
+])
+def test_layer_streaming_kernel_shapes(T, H, I, E, k, ep, fp8):
+    announce(f"streaming-kernel shape T={T} H={H} I={I} E={E} k={k} ep={ep} fp8={fp8}")
+    L = Layer(config=94, T=T, H=H, I=I, E=E, k=k, fp8=fp8, ep_size=ep, ep_rank=ep - 1)
+    check_layer(L, n_sample=10 ** 6)
+
+
 @pytest.mark.parametrize("T", [1, 8, 32, 128, 256, 512, 1024, 4096])
 def test_bf16_layer_2048x768_e128_top8_uniform(T):
     announce(f"bf16 H=2048 I=768 E=128 k=8 uniform T={T}")
