@@ -88,8 +88,10 @@ typedef struct {
     int32_t m_tiles;         /* row tiles of the grouped GEMMs (light + heavy)              */
     int32_t rows_estimate;   /* host plan: max(1, ceil(T*top_k/E))                          */
     int32_t tile_rows;       /* host plan: largest light tile (one per expert with 1..tile_rows
-                                rows); heavier experts get tiles of at most 128 rows         */
+                                rows); heavier experts are cut into heavy tiles              */
     int32_t heavy_tiles;     /* row tiles of experts with more than tile_rows rows           */
+    int32_t heavy_rows;      /* host plan: rows of a full heavy tile (an expert with c rows
+                                gets c / heavy_rows full tiles and one with the rest)        */
 } fmoe_stats;
 
 int fmoe_abi_version(void);

@@ -31,13 +31,19 @@ def flags() -> list[str]:
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
 
 
+# per-source extra flags: the heavy kernel keeps MFMA accumulators in ordinary VGPRs (its
+# register budget at two wavefronts per SIMD holds them, and the accumulator-register form
+# makes the compiler copy them between register files every loop iteration)
+EXTRA_FLAGS = {"gemm_heavy.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     cc = hipcc()
 
     def compile_one(src: str) -> str:
         obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -40,6 +40,7 @@ struct Plan {
     long long n;         // T*k assignments
     int rows_estimate;   // max(1, ceil(T*k/E))
     int tile_rows;       // largest light row tile: 16 or 32 (heavier experts use heavy tiles)
+    int heavy_rows;      // rows of a full heavy tile
     int max_light;       // bounds on light and heavy row tiles for any routing
     int max_heavy;
     int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
@@ -96,7 +97,8 @@ Plan make_plan(const fmoe_shape* s) {
     // light tiles: one per expert with 1..tile_rows rows; heavy tiles: ceil(c/128) per expert
     // with c > tile_rows rows, at most n/128 + (n / (tile_rows + 1)) in all; no tile is empty
     const long long nl = p.El < p.n ? p.El : p.n;
-    long long nh = p.n / kHeavyRows + (p.n / (tr + 1) < p.El ? p.n / (tr + 1) : p.El) + 1;
+    p.heavy_rows = heavy_max_rows(p.fp8);
+    long long nh = p.n / p.heavy_rows + (p.n / (tr + 1) < p.El ? p.n / (tr + 1) : p.El) + 1;
     if (nh > p.n) nh = p.n;
     p.max_light = (int)(nl < 1 ? 1 : nl);
     p.max_heavy = (int)(nh < 1 ? 1 : nh);
@@ -179,7 +181,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
 
     record(ev, FMOE_STAGE_GROUP, st);
     MTile* mtiles_heavy = mtiles + p.max_light;
-    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, (int32_t*)(ws + L.counts),
+    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.heavy_rows, p.rows_estimate, (int32_t*)(ws + L.counts),
                           (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
                           mtiles_heavy, hdr, st));
     // an expert can hold more than tile_rows rows only if there are more assignments than that
@@ -325,7 +327,7 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
     char* wsb = (char*)ws;
     MTile* mt = (MTile*)(wsb + p.L.mtiles);
-    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.rows_estimate, counts, offsets,
+    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.heavy_rows, p.rows_estimate, counts, offsets,
                                    perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp), mt,
                                    mt + p.max_light, (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
 }
@@ -372,6 +374,7 @@ int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {
     out->empty_experts = h.empty_experts;
     out->m_tiles = h.m_tiles + h.m_tiles_heavy;
     out->heavy_tiles = h.m_tiles_heavy;
+    out->heavy_rows = h.heavy_rows;
     out->tile_rows = h.tile_rows;
     out->rows_estimate = h.rows_estimate;
     return FMOE_OK;

@@ -14,7 +14,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr float kE4M3Max = 448.0f;  // largest finite OCP E4M3FN magnitude
 constexpr int kMaxKBlocks = 512;    // 128-deep blocks of the reduction dimension (65536 / 128)
 constexpr int kLightRows = 32;      // largest row tile of the light GEMM kernel
-constexpr int kHeavyRows = 256;     // largest row tile of the heavy GEMM kernel
+// largest row tile of the heavy GEMM kernel: 256 rows (16 sub-blocks of 16) for bf16 weights;
+// 128 for FP8, whose per-step operands and scaled accumulation leave registers for 8 sub-blocks
+constexpr int heavy_max_rows(bool fp8) { return fp8 ? 128 : 256; }
 
 // Workspace header written by the grouping kernel and read by later kernels and by
 // fmoe_read_stats.  Field order is part of the workspace format of this library only.
@@ -27,7 +29,8 @@ struct DevHeader {
     int32_t tile_rows;      // largest rows per tile used to cut the experts
     int32_t rows_estimate;  // max(1, ceil(T*top_k/E)) of the host plan
     int32_t m_tiles_heavy;  // heavy row tiles (experts with more than tile_rows rows)
-    int32_t pad[7];
+    int32_t heavy_rows;     // rows of a full heavy tile
+    int32_t pad[6];
 };
 static_assert(sizeof(DevHeader) == 64, "header size");
 

@@ -1,20 +1,33 @@
-// gemm_heavy.hip -- grouped expert GEMMs for heavy row tiles (33..256 rows of one expert).
+// gemm_heavy.hip -- grouped expert GEMMs for heavy row tiles (more rows than a light tile, at
+// most 256 rows of one expert).
 //
 // Same operation as gemm.hip (gate/up with SiLU-and-mul, or down; bf16 or FP8 block-scaled),
-// for experts that hold more rows than the light kernel's 32: large batches, and the hot
-// experts of a concentrated routing ("vLLM Community Traces H20 MoE Scheduling Inefficiency
-// to Expert-Load Kernel Selection", paragraph 4: concentrated routing needs another kernel
-// choice than the average).
+// for experts that hold more rows than a light tile: large batches, and the hot experts of a
+// concentrated routing ("vLLM Community Traces H20 MoE Scheduling Inefficiency to
+// Expert-Load Kernel Selection", paragraph 4: concentrated routing needs another kernel choice
+// than the average).
 //
-// Shape: a workgroup owns one row tile (up to 256 rows = 16 sub-blocks of 16) and 128 output
-// features; each of its 4 wavefronts owns 32 features (two 16-row weight blocks per matrix)
-// and all the tile's rows.  The tile's activation rows are staged through LDS in chunks of
-// 256 bytes per row (128 bf16 or 256 e4m3 along the reduction), double-buffered and shared by
-// the 4 wavefronts, so each activation byte crosses L2 once per workgroup instead of once per
-// wavefront.  Weights are streamed from HBM straight into registers (a ring of D MFMA steps)
-// as in the light kernel, and every weight fragment feeds up to 16 sub-blocks of MFMAs, so a
-// 256-row tile reads each weight of its 128 features once.  A chunk's MFMA work (about 4k
-// cycles at 256 rows) covers the latency of the next chunk's loads.
+// Shape: a workgroup of 8 wavefronts owns one row tile and 128 output features; wavefront v
+// takes 16 of the features (two weight matrices' worth for gate/up) for all of the tile's rows,
+// so every weight fragment it holds feeds up to 16 sub-blocks of 16 rows, a 256-row tile reads
+// its weights from HBM once, and every weight byte is loaded by one wavefront only.  Two
+// wavefronts per SIMD keep the matrix cores fed while the other waits.
+//
+// Weights stream from HBM straight into registers (the MFMA "A" operand, a ring of D steps per
+// wavefront).  The tile's activation rows (the "B" operand) are staged in LDS by direct
+// global-to-LDS loads: each load instruction gathers one 16-row x 64-byte MFMA fragment (rows
+// through the gather map) and writes it in the order the MFMA reads it (lane i at byte 16 i),
+// so reads are contiguous and conflict free.  Four chunk buffers are kept, three chunks ahead
+// of the one being read, so the gathers (served by L2 or the Infinity Cache) never hold up the
+// stream.  Each buffer is a separate LDS array, so the compiler knows that a read of one
+// buffer does not depend on loads still landing in another; the waits before each step and
+// each chunk are explicit counts of the loads that must have arrived.
+//
+// FP8 (e4m3 weights with one fp32 scale per [128,128] block, activations with one fp32 scale
+// per row and 128 columns): one v_mfma_f32_16x16x128_f8f6f4 covers one 128-deep scale block;
+// its exact product is added to the fp32 accumulator times (weight scale * activation scale).
+// The tile's weight scales are read into LDS once per tile, the activation scales of a chunk
+// are staged with it.
 #include <type_traits>
 
 #include "launch.hpp"
@@ -23,259 +36,296 @@ namespace fmoe {
 
 namespace {
 
-constexpr int kHeavyFeatures = 128;        // output features per workgroup (4 x 32)
-constexpr int kChunkBytes = 256;           // bytes per activation row per chunk
-constexpr int kRowStride = kChunkBytes + 16;  // LDS row stride: conflict-free 16-byte reads
-
-__device__ __forceinline__ float silu_mul_h(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+constexpr int kHvFeatures = 128;  // output features per workgroup: 8 wavefronts x 16
+constexpr int kHvThreads = 512;
+constexpr int kHvFrags = 32;      // 1 KB fragment pieces per chunk buffer
 
 template <bool FP8>
-struct HCfg {
+struct HvCfg {
     using T = bf16x8;
     static constexpr int KSTEP = 32;   // reduction depth of one MFMA
     static constexpr int EB = 2;       // bytes per element
-    static constexpr int FRAG = 16;    // bytes per lane per operand
-    static constexpr int D = 4;        // weight ring depth (steps)
+    static constexpr int LANE_B = 16;  // operand bytes per lane per step
+    static constexpr int HALVES = 1;   // 16-byte pieces per lane fragment
+    static constexpr int CS = 2;       // steps per staged chunk
 };
 template <>
-struct HCfg<true> {
+struct HvCfg<true> {
     using T = i32x8;
     static constexpr int KSTEP = 128;
     static constexpr int EB = 1;
-    static constexpr int FRAG = 32;
-    static constexpr int D = 2;
+    static constexpr int LANE_B = 32;
+    static constexpr int HALVES = 2;
+    static constexpr int CS = 1;
 };
 
-struct HeavyLds {
-    uint8_t tok[2][kHeavyRows][kRowStride];  // activation chunks
-    float asc[2][kHeavyRows][2];             // FP8: activation scales of the chunk's 2 k-blocks
-    float wsc[2][kMaxKBlocks];               // FP8: weight-block scales (gate, up) of the tile
-    int src[kHeavyRows];                     // activation row of each tile row
-};
+__device__ __forceinline__ float silu_mul_h(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-template <bool FP8>
-__device__ __forceinline__ typename HCfg<FP8>::T lds_frag(const uint8_t* p) {
-    if constexpr (FP8) {
-        const i32x4 a = *(const i32x4*)p;
-        const i32x4 b = *(const i32x4*)(p + 16);
-        return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    } else {
-        return *(const bf16x8*)p;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// compiler-only fence: no memory access moves across it; emits nothing
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
     }
 }
 
-template <bool FP8>
-__device__ __forceinline__ typename HCfg<FP8>::T gl_frag(const uint8_t* p) {
-    if constexpr (FP8) return *(const i32x8*)p;
-    else return *(const bf16x8*)p;
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cap63(int n) { return n > 63 ? 63 : n; }
+
+// Vector-memory instructions certainly issued after the weight loads of the step at position p
+// (0 <= p < 4 CS) of the four-chunk loop body, when that step is computed.  A step's loads are
+// issued right after the step D earlier is computed; after them come the weight loads of the
+// D-1 steps in between and the staging group at the start of every chunk entered since (in the
+// first pass, steps p < D were loaded in the prologue, after which only the groups of chunks
+// 0..p/CS follow).
+template <int p, int CS, int D, int WL, int QD>
+constexpr int weight_wait() {
+    constexpr int crossed = (p + 4 * CS) / CS - (p + 4 * CS - D) / CS;
+    return cap63((D - 1) * WL + QD * cmin(crossed, p / CS + 1));
 }
 
-template <bool GATED, bool FP8, bool OUT_F32, int NS>
-__device__ __forceinline__ void heavy_tile(const GemmArgs& g, const MTile& m, int nb, HeavyLds& L) {
-    using C = HCfg<FP8>;
-    using FT = typename C::T;
-    constexpr int NW = GATED ? 2 : 1;
-    constexpr int FB = 2;                               // 16-row weight blocks per wavefront
-    constexpr int CS = kChunkBytes / (C::KSTEP * C::EB);  // MFMA steps per chunk: 4 (bf16) / 2 (fp8)
-    // weight ring depth in MFMA steps: deep enough to cover HBM latency under load; smaller
-    // when the tile's accumulators leave fewer registers
-    constexpr int D = FP8 ? C::D : (NS >= 16 ? C::D : 2 * C::D);
-    constexpr int PIECES = NS * 16 * (kChunkBytes / 16) / 256;  // 16-byte staging pieces per thread
-    static_assert((2 * CS) % D == 0, "ring slots repeat every pair of chunks");
-    const int lane = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r16 = lane & 15, kg = lane >> 4;
-    const int K = g.K;
-    const int nsteps = K / C::KSTEP;
-    const int nchunks = (nsteps + CS - 1) / CS;
-    const int nkb = K >> 7;
-    const size_t rowbytes = (size_t)K * C::EB;
-    const int f0 = nb * kHeavyFeatures + w * 32;  // this wavefront's first feature
-
-    // weights: lane row r16 of block fb, bytes kg*FRAG of each step
-    const uint8_t* wbase0 = (const uint8_t*)g.W0 + ((size_t)m.expert * g.N + f0 + r16) * rowbytes + kg * C::FRAG;
-    const uint8_t* wbase1 = GATED ? (const uint8_t*)g.W1 + ((size_t)m.expert * g.N + f0 + r16) * rowbytes + kg * C::FRAG
-                                  : wbase0;
-    const size_t fbstride = 16 * rowbytes;
-    FT bw[D][FB][NW];
-    auto issue_w = [&](int slot, int step) {
-        const size_t o = (size_t)step * C::KSTEP * C::EB;
-#pragma unroll
-        for (int fb = 0; fb < FB; fb++) {
-            bw[slot][fb][0] = gl_frag<FP8>(wbase0 + fb * fbstride + o);
-            if constexpr (GATED) bw[slot][fb][NW - 1] = gl_frag<FP8>(wbase1 + fb * fbstride + o);
-        }
-    };
-
-    // staging: thread t owns 16-byte piece (t & 15) of rows (t >> 4) + 16j, j < PIECES.  In LDS
-    // the pieces of a row are stored transposed (step-minor): piece q = step*PP + j goes to
-    // position j*CS + step, so the 16-byte reads of one MFMA step (lane = 16*kg + row) fall in
-    // 16 distinct 4-bank groups for any grouping of 16 lanes by row or by kg.
-    constexpr int COLS = kChunkBytes / 16;
-    constexpr int PP = COLS / CS;  // pieces per MFMA step in a row
-    const int scol = threadIdx.x % COLS, srow0 = threadIdx.x / COLS;
-    const int spos = (scol % PP) * CS + scol / PP;
-    i32x4 stage[PIECES];
-    float sstage[2];
-    auto load_chunk = [&](int c) {
-        // the last chunk may be partial: columns past the row end re-read the row's last 16 bytes
-        const size_t col = min((size_t)c * kChunkBytes + scol * 16, rowbytes - 16);
-#pragma unroll
-        for (int j = 0; j < PIECES; j++)
-            stage[j] = *(const i32x4*)((const uint8_t*)g.A + (size_t)L.src[srow0 + (256 / COLS) * j] * rowbytes + col);
-        if constexpr (FP8) {
-            // activation scales of the chunk's 2 k-blocks: 16*NS rows x 2 entries
-#pragma unroll
-            for (int q = 0; q < 2; q++) {
-                const int e = threadIdx.x + 256 * q;
-                const int r = e >> 1, kb = min(c * 2 + (e & 1), nkb - 1);
-                sstage[q] = (r < NS * 16) ? g.A_scale[(size_t)L.src[r] * nkb + kb] : 0.0f;
-            }
-        }
-    };
-    auto store_chunk = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < PIECES; j++) *(i32x4*)&L.tok[buf][srow0 + (256 / COLS) * j][spos * 16] = stage[j];
-        if constexpr (FP8) {
-#pragma unroll
-            for (int q = 0; q < 2; q++) {
-                const int e = threadIdx.x + 256 * q;
-                if ((e >> 1) < NS * 16) L.asc[buf][e >> 1][e & 1] = sstage[q];
-            }
-        }
-    };
-
-    f32x4 acc[NS][FB][NW];
-#pragma unroll
-    for (int sb = 0; sb < NS; sb++)
-#pragma unroll
-        for (int fb = 0; fb < FB; fb++)
-#pragma unroll
-            for (int h = 0; h < NW; h++) acc[sb][fb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int d = 0; d < D; d++) issue_w(d, min(d, nsteps - 1));
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-
-    // one chunk: prefetch the next chunk into registers, run its MFMA steps from LDS buffer B,
-    // then publish the prefetched chunk in the other buffer
-    auto run_chunk = [&](auto Bc, int c) {
-        constexpr int B = decltype(Bc)::value;
-        load_chunk(min(c + 1, nchunks - 1));  // next chunk (the last one re-reads itself)
-#pragma unroll
-        for (int s = 0; s < CS; s++) {
-            const int step = c * CS + s;
-            const int slot = (B * CS + s) % D;
-            if (step < nsteps) {
-#pragma unroll
-                for (int sb = 0; sb < NS; sb++) {
-                    const uint8_t* row = &L.tok[B][sb * 16 + r16][0];
-                    if constexpr (!FP8) {
-                        const FT xb = lds_frag<FP8>(row + (kg * CS + s) * 16);
-#pragma unroll
-                        for (int fb = 0; fb < FB; fb++)
-#pragma unroll
-                            for (int h = 0; h < NW; h++)
-                                acc[sb][fb][h] =
-                                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[slot][fb][h], xb, acc[sb][fb][h], 0, 0, 0);
-                    } else {
-                        const i32x4 lo = *(const i32x4*)(row + ((2 * kg) * CS + s) * 16);
-                        const i32x4 hi = *(const i32x4*)(row + ((2 * kg + 1) * CS + s) * 16);
-                        const FT xb = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        const float sa = L.asc[B][sb * 16 + r16][s];
-                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int h = 0; h < NW; h++) {
-                            const float cs = L.wsc[h][step] * sa;
-#pragma unroll
-                            for (int fb = 0; fb < FB; fb++) {
-                                const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[slot][fb][h], xb, zero,
-                                                                                                  0, 0, 0, 0, 0, 0);
-#pragma unroll
-                                for (int i = 0; i < 4; i++) acc[sb][fb][h][i] = __builtin_fmaf(p[i], cs, acc[sb][fb][h][i]);
-                            }
-                        }
-                    }
-                }
-            }
-            issue_w(slot, min(step + D, nsteps - 1));
-        }
-        store_chunk(B ^ 1);
-        __syncthreads();
-    };
-    for (int c = 0; c < nchunks; c += 2) {
-        run_chunk(std::integral_constant<int, 0>{}, c);
-        if (c + 1 < nchunks) run_chunk(std::integral_constant<int, 1>{}, c + 1);
-    }
-
-    // epilogue: lane holds token column sb*16 + r16, features f0 + fb*16 + kg*4 + i
-#pragma unroll
-    for (int sb = 0; sb < NS; sb++) {
-        const int c = sb * 16 + r16;
-        if (c >= m.rows) continue;
-#pragma unroll
-        for (int fb = 0; fb < FB; fb++) {
-            const size_t o = (size_t)(m.row0 + c) * g.N + f0 + fb * 16 + kg * 4;
-            float r[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_h(acc[sb][fb][0][i], acc[sb][fb][NW - 1][i]) : acc[sb][fb][0][i];
-            if (OUT_F32) {
-                *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
-            } else {
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-                *(uint2*)((uint16_t*)g.out + o) = pk;
-            }
-        }
-    }
+template <bool GATED, bool FP8>
+constexpr int ring_depth() {
+    return FP8 ? (GATED ? 2 : 4) : (GATED ? 8 : 8);
 }
 
 template <bool GATED, bool FP8, bool OUT_F32>
-__global__ __launch_bounds__(256) void k_grouped_gemm_heavy(GemmArgs g) {
-    __shared__ HeavyLds L;
-    const int nblocks = g.N / kHeavyFeatures;
+__global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
+    using C = HvCfg<FP8>;
+    using FT = typename C::T;
+    constexpr int NW = GATED ? 2 : 1;
+    constexpr int CS = C::CS;
+    constexpr int D = ring_depth<GATED, FP8>();
+    constexpr int WL = NW * (FP8 ? 2 : 1);  // weight load instructions per step
+    static_assert(4 * CS % D == 0, "ring slots repeat every four chunks");
+
+    // four chunk buffers, each its own LDS array (see the header)
+    __shared__ i32x4 X0[kHvFrags * 64], X1[kHvFrags * 64], X2[kHvFrags * 64], X3[kHvFrags * 64];
+    __shared__ float A0[FP8 ? 256 : 1], A1[FP8 ? 256 : 1], A2[FP8 ? 256 : 1], A3[FP8 ? 256 : 1];
+    __shared__ float WS[2][FP8 ? kMaxKBlocks : 1];
+
+    const int lane = lane_id();
+    const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int K = g.K;
+    const int nsteps = K / C::KSTEP;
+    const int nkb = K >> 7;
+    const int nch = (nsteps + CS - 1) / CS;
+    const size_t rowbytes = (size_t)K * C::EB;
+    const int nblocks = g.N / kHvFeatures;
     const int total = *g.tile_count * nblocks;
-    const int nkb = g.K >> 7;
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const int mt = tile / nblocks;
-        const int nb = tile - mt * nblocks;
-        const MTile m = g.mtiles[mt];
-        const int nsub = (m.rows + 15) >> 4;
-        const int NSr = nsub <= 4 ? 4 : (nsub <= 8 ? 8 : 16);
-        if (threadIdx.x < NSr * 16) {
-            const int p = m.row0 + min((int)threadIdx.x, m.rows - 1);
-            L.src[threadIdx.x] = g.perm_src ? g.perm_src[p] / g.topk : p;
-        }
+    const int topk = g.perm_src ? g.topk : 1;
+
+    for (int task = blockIdx.x; task < total; task += gridDim.x) {
+        const int mt = task / nblocks;
+        const int nb = task - mt * nblocks;
+        // the tile list is read-only here: a scalar load through the constant address space
+        const i32x4 mv = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + mt);
+        const int expert = mv[0], row0 = mv[1], rows = mv[2];
+
+        // one tile of NS sub-blocks of 16 rows
+        auto run = [&](auto NSc) {
+            constexpr int NS = decltype(NSc)::value;
+            constexpr int F = CS * NS * C::HALVES;       // fragment pieces per chunk
+            constexpr int QX = F >= 8 ? F / 8 : 1;       // staging loads per wavefront per chunk
+            constexpr int QD = QX + (FP8 ? 1 : 0);       // with the activation-scale load
+            constexpr int NWAIT = cap63(2 * QD + cmin(2 * CS, D + CS) * WL);
+            constexpr int NPRO = cap63(2 * QD + D * WL);
+
+            // staging sources: wavefront v loads pieces (v*QX + j) mod F; piece f is step
+            // f / (NS HALVES) of the chunk, sub-block (f / HALVES) % NS, half f % HALVES (waves
+            // past the F pieces repeat one, writing the same bytes to the same place)
+            size_t xoff[QX];
+            int xstep[QX], xpos[QX];
+#pragma unroll
+            for (int j = 0; j < QX; j++) {
+                const int f = (v * QX + j) % F;
+                const int sb = (f / C::HALVES) % NS;
+                const int p = row0 + min(sb * 16 + r16, rows - 1);
+                const int src = (g.perm_src ? g.perm_src[p] : p) / topk;
+                xoff[j] = (size_t)src * rowbytes + kg * C::LANE_B + (f % C::HALVES) * 16;
+                xstep[j] = f / (NS * C::HALVES);
+                xpos[j] = f * 64;
+            }
+            // FP8 activation scales of a chunk: entry e = (v*64 + lane) mod 16 NS is tile row e
+            int ascale_src = 0;
+            if constexpr (FP8) {
+                const int e = (v * 64 + lane) % (16 * NS);
+                const int p = row0 + min(e, rows - 1);
+                ascale_src = (g.perm_src ? g.perm_src[p] : p) / topk;
+            }
+            auto stage = [&](auto Bc, int c) {
+                constexpr int B = decltype(Bc)::value;
+                i32x4* X = B == 0 ? X0 : B == 1 ? X1 : B == 2 ? X2 : X3;
+#pragma unroll
+                for (int j = 0; j < QX; j++) {
+                    const size_t step = (size_t)min(c * CS + xstep[j], nsteps - 1);
+                    __builtin_amdgcn_global_load_lds(
+                        (gbl_void*)((const uint8_t*)g.A + xoff[j] + step * (C::KSTEP * C::EB)),
+                        (lds_void*)(X + xpos[j]), 16, 0, 0);
+                }
+                if constexpr (FP8) {
+                    float* A = B == 0 ? A0 : B == 1 ? A1 : B == 2 ? A2 : A3;
+                    const int kb = min(c, nkb - 1);  // CS = 1: chunk c is 128-deep block c
+                    __builtin_amdgcn_global_load_lds((gbl_void*)(g.A_scale + (size_t)ascale_src * nkb + kb),
+                                                     (lds_void*)(A + ((v * 64) % (16 * NS))), 4, 0, 0);
+                }
+            };
+
+            // weights: lane row r16 of this wavefront's 16 features
+            const size_t wrow = (size_t)expert * g.N + nb * kHvFeatures + v * 16 + r16;
+            const uint8_t* wp[NW];
+            wp[0] = (const uint8_t*)g.W0 + wrow * rowbytes + kg * C::LANE_B;
+            if constexpr (GATED) wp[NW - 1] = (const uint8_t*)g.W1 + wrow * rowbytes + kg * C::LANE_B;
+            FT bw[D][NW];
+            auto issue_w = [&](int slot, int step) {
+                const size_t o = (size_t)min(step, nsteps - 1) * (C::KSTEP * C::EB);
+#pragma unroll
+                for (int h = 0; h < NW; h++) bw[slot][h] = *(const FT*)(wp[h] + o);
+            };
+
+            f32x4 acc[NS][NW];
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++)
+#pragma unroll
+                for (int h = 0; h < NW; h++) acc[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            // step s of the chunk in buffer B, weights from ring slot `slot`
+            auto compute = [&](auto Bc, int slot, int s, int step) {
+                constexpr int B = decltype(Bc)::value;
+                const i32x4* X = B == 0 ? X0 : B == 1 ? X1 : B == 2 ? X2 : X3;
+#pragma unroll
+                for (int sb = 0; sb < NS; sb++) {
+                    if constexpr (!FP8) {
+                        const bf16x8 xb = __builtin_bit_cast(bf16x8, X[(s * NS + sb) * 64 + lane]);
+#pragma unroll
+                        for (int h = 0; h < NW; h++)
+                            acc[sb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[slot][h], xb, acc[sb][h], 0, 0, 0);
+                    } else {
+                        const float* A = B == 0 ? A0 : B == 1 ? A1 : B == 2 ? A2 : A3;
+                        const i32x4 lo = X[(sb * 2) * 64 + lane];
+                        const i32x4 hi = X[(sb * 2 + 1) * 64 + lane];
+                        const i32x8 xb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        const float sa = A[sb * 16 + r16];
+                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int h = 0; h < NW; h++) {
+                            const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[slot][h], xb, zero,
+                                                                                               0, 0, 0, 0, 0, 0);
+                            const float cs = WS[h][step] * sa;
+#pragma unroll
+                            for (int i = 0; i < 4; i++) acc[sb][h][i] = __builtin_fmaf(pr[i], cs, acc[sb][h][i]);
+                        }
+                    }
+                    // interleave: one fragment read ahead of the matrix operations that use it
+                    __builtin_amdgcn_sched_group_barrier(0x100, C::HALVES, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, NW, 0);
+                }
+            };
+
+            // prologue: chunks 0..2 in flight, D weight steps in flight, chunk 0 landed
+            __builtin_amdgcn_sched_barrier(0);
+            stage(std::integral_constant<int, 0>{}, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            stage(std::integral_constant<int, 1>{}, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            stage(std::integral_constant<int, 2>{}, 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = 0; d < D; d++) issue_w(d, d);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<NPRO>();
+            compiler_fence();
+            __builtin_amdgcn_s_barrier();
+            compiler_fence();
+            __builtin_amdgcn_sched_barrier(0);
+
+            // chunk c from buffer B: stage chunk c+3 into the buffer read last, run the chunk's
+            // steps, then wait for chunk c+1 and for every wavefront to be done with chunk c
+            auto chunk = [&](auto Bc, int c) {
+                constexpr int B = decltype(Bc)::value;
+                stage(std::integral_constant<int, (B + 3) & 3>{}, c + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0, CS>([&](auto Sc) {
+                    constexpr int s = decltype(Sc)::value;
+                    constexpr int slot = (B * CS + s) % D;
+                    const int step = c * CS + s;
+                    // this step's weights have landed (an explicit count: with global-to-LDS
+                    // loads in flight the compiler would otherwise wait for everything)
+                    wait_vmcnt<weight_wait<B * CS + s, CS, D, WL, QD>()>();
+                    if (step < nsteps) compute(Bc, slot, s, step);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_w(slot, step + D);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                wait_vmcnt<NWAIT>();
+                compiler_fence();
+                __builtin_amdgcn_s_barrier();
+                compiler_fence();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // whole groups of four chunks (an early exit would cost the exact wait counts the
+            // compiler keeps across the loop); chunks past the end load clamped addresses and
+            // compute nothing
+            for (int c0 = 0; c0 < nch; c0 += 4) {
+                chunk(std::integral_constant<int, 0>{}, c0);
+                chunk(std::integral_constant<int, 1>{}, c0 + 1);
+                chunk(std::integral_constant<int, 2>{}, c0 + 2);
+                chunk(std::integral_constant<int, 3>{}, c0 + 3);
+            }
+
+            // epilogue: lane holds tile row sb*16 + r16 and features nb*128 + v*16 + kg*4 + i
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++) {
+                const int col = sb * 16 + r16;
+                if (col >= rows) continue;
+                const size_t o = (size_t)(row0 + col) * g.N + nb * kHvFeatures + v * 16 + kg * 4;
+                float r[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_h(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
+                if (OUT_F32) {
+                    *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
+                } else {
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+                    pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+                    *(uint2*)((uint16_t*)g.out + o) = pk;
+                }
+            }
+        };
+
         if constexpr (FP8) {
             // the workgroup's 128 features are one 128-row weight block
-            const size_t srow = ((size_t)m.expert * (g.N >> 7) + nb) * nkb;
-            for (int q = threadIdx.x; q < nkb; q += 256) {
-                L.wsc[0][q] = g.S0[srow + q];
-                if (GATED) L.wsc[1][q] = g.S1[srow + q];
+            const size_t srow = ((size_t)expert * (g.N >> 7) + nb) * nkb;
+            for (int q = threadIdx.x; q < nkb; q += kHvThreads) {
+                WS[0][q] = g.S0[srow + q];
+                if (GATED) WS[1][q] = g.S1[srow + q];
             }
         }
+        // every load of the previous tile has landed (its last staging loads ran past its end)
+        // and every wavefront is past it, so the staging buffers are free; the weight scales are
+        // visible
+        wait_vmcnt<0>();
         __syncthreads();
-        if (nsub <= 4) {
-            heavy_tile<GATED, FP8, OUT_F32, 4>(g, m, nb, L);
-        } else if (nsub <= 8) {
-            heavy_tile<GATED, FP8, OUT_F32, 8>(g, m, nb, L);
-        } else if constexpr (GATED) {
-            // 256 gate/up accumulators would not leave registers for the rest: two 128-row
-            // halves, the second re-reading the tile's weights from cache
-            MTile a = m, b = m;
-            a.rows = 128;
-            b.row0 = m.row0 + 128;
-            b.rows = m.rows - 128;
-            heavy_tile<GATED, FP8, OUT_F32, 8>(g, a, nb, L);
-            if (threadIdx.x < 128) L.src[threadIdx.x] = L.src[128 + threadIdx.x];
-            __syncthreads();
-            heavy_tile<GATED, FP8, OUT_F32, 8>(g, b, nb, L);
-        } else {
-            heavy_tile<GATED, FP8, OUT_F32, 16>(g, m, nb, L);
-        }
+        const int nsub = (rows + 15) >> 4;  // sub-blocks of 16 rows
+        if (nsub > 8) {
+            if constexpr (heavy_max_rows(FP8) > 128) run(std::integral_constant<int, 16>{});
+        } else if (nsub > 4) run(std::integral_constant<int, 8>{});
+        else if (nsub > 2) run(std::integral_constant<int, 4>{});
+        else if (nsub > 1) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
     }
 }
 
@@ -284,16 +334,16 @@ hipError_t launch_heavy(const GemmArgs& a, int max_tiles, int cus, hipStream_t s
     static int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_heavy<GATED, FP8, OUT_F32>, 256, 0) !=
-                hipSuccess || nb < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_heavy<GATED, FP8, OUT_F32>, kHvThreads,
+                                                          0) != hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
     }
-    long long grid = (long long)max_tiles * (a.N / kHeavyFeatures);
+    long long grid = (long long)max_tiles * (a.N / kHvFeatures);
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    k_grouped_gemm_heavy<GATED, FP8, OUT_F32><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_grouped_gemm_heavy<GATED, FP8, OUT_F32><<<(unsigned)grid, kHvThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 

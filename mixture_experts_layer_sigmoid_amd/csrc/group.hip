@@ -106,7 +106,8 @@ __device__ int block_max(int v, int* sh) {
 // the header.  Thread t works on expert e = t % El' and part p = t / El' of its chunks
 // (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
 // threads read consecutive experts of a chunk.
-__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int rows_estimate, long long dropped,
+__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int heavy_rows, int rows_estimate,
+                              long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
                               int* sh /* >= kScanShared ints */) {
@@ -139,10 +140,10 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int r
         total += v;
     }
     const int lead = (live && part == 0);
-    // an expert with 1..tile_rows rows is one light tile; a heavier one is cut into heavy
-    // tiles of at most kHeavyRows rows
+    // an expert with 1..tile_rows rows is one light tile; a heavier one is cut into full heavy
+    // tiles of heavy_rows rows and one tile with the rest
     const bool heavy = total > tile_rows;
-    const int nheavy = heavy ? (total + kHeavyRows - 1) / kHeavyRows : 0;
+    const int nheavy = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
     int R, n_light, n_heavy, empty;
     const int first = block_scan_excl(lead ? total : 0, sh, &R);  // valid in the lead thread
     const int lfirst = block_scan_excl(lead && total > 0 && !heavy, sh, &n_light);
@@ -196,12 +197,11 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int r
             mtiles[my_lfirst] = mt;
         }
         if (heavy) {
-            const int per_tile = ((total + nheavy - 1) / nheavy + 15) / 16 * 16;  // even split, 16-row steps
             for (int j = part; j < nheavy; j += P) {
                 MTile mt;
                 mt.expert = e;
-                mt.row0 = my_first + j * per_tile;
-                mt.rows = min(per_tile, total - j * per_tile);
+                mt.row0 = my_first + j * heavy_rows;
+                mt.rows = min(heavy_rows, total - j * heavy_rows);
                 mt.pad = 0;
                 mtiles_heavy[my_hfirst + j] = mt;
             }
@@ -216,6 +216,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int r
         hdr->empty_experts = empty;
         hdr->dropped = dropped;
         hdr->tile_rows = tile_rows;
+        hdr->heavy_rows = heavy_rows;
         hdr->rows_estimate = rows_estimate;
     }
 }
@@ -236,7 +237,7 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 // ---------------------------------------------------------------- one-workgroup path
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
-                                                             int lo, int tile_rows, int rows_estimate,
+                                                             int lo, int tile_rows, int heavy_rows, int rows_estimate,
                                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
                                                              int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
     __syncthreads();
     long long dropped = 0;
     for (int c = 0; c < nchunk; c++) dropped += bads[c];
-    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
     __syncthreads();
     if (w < nchunk) chunk_scatter(w * 64 + lane_id(), n, l, r, l >= 0 ? cnt[w * El + l] : 0, perm_src, inv_perm);
 }
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int rows_estimate, const int* __restrict__ bad_buf,
+                                                            int heavy_rows, int rows_estimate,
+                                                            const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
                                                             DevHeader* __restrict__ hdr) {
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
 }
 
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
@@ -312,20 +314,23 @@ size_t group_scratch_bytes(long long n, int El) {
     return (size_t)(nchunk * El + nchunk) * sizeof(int);
 }
 
-hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int rows_estimate,
+hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
+                        int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
     const size_t lds = (size_t)(2 * El * nchunk + kSmallChunks + kScanShared) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
-        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, rows_estimate, counts, offsets,
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts,
+                                                    offsets,
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
         return hipGetLastError();
     }
     int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, rows_estimate, bad, counts, offsets, mtiles,
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, bad, counts,
+                                             offsets, mtiles,
                                              mtiles_heavy, hdr);
     k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);
     return hipGetLastError();
