@@ -153,8 +153,11 @@ int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int
 
 /* Stages of fmoe_forward, in launch order, for fmoe_forward_profiled. */
 enum {
-    FMOE_STAGE_ROUTER = 0, FMOE_STAGE_GROUP = 1, FMOE_STAGE_QUANT_X = 2, FMOE_STAGE_GEMM1 = 3,
-    FMOE_STAGE_QUANT_H = 4, FMOE_STAGE_GEMM2 = 5, FMOE_STAGE_COMBINE = 6, FMOE_NUM_STAGES = 7
+    FMOE_STAGE_ROUTER = 0, FMOE_STAGE_GROUP = 1, FMOE_STAGE_QUANT_X = 2,
+    FMOE_STAGE_GEMM1 = 3,        /* gate/up GEMM of the light row tiles                       */
+    FMOE_STAGE_GEMM1_HEAVY = 4,  /* gate/up GEMM of the heavy row tiles (may find none)       */
+    FMOE_STAGE_QUANT_H = 5, FMOE_STAGE_GEMM2 = 6, FMOE_STAGE_GEMM2_HEAVY = 7, FMOE_STAGE_COMBINE = 8,
+    FMOE_NUM_STAGES = 9
 };
 
 /* fmoe_forward that also records stage_events[i] (hipEvent_t, created by the caller) on the

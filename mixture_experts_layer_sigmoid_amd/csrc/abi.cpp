@@ -207,6 +207,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g1.tile_count = &hdr->m_tiles;
     if (p.wk1 == 1) FMOE_TRY(launch_grouped_gemm_stream(true, p.fp8, p.fp8, g1, p.tile_rows, p.max_light, cus, st));
     else FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_light, cus, st));
+    record(ev, FMOE_STAGE_GEMM1_HEAVY, st);
     if (heavy_possible) {
         GemmArgs g1h = g1;
         g1h.mtiles = mtiles_heavy;
@@ -235,6 +236,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g2.tile_count = &hdr->m_tiles;
     if (p.wk2 == 1) FMOE_TRY(launch_grouped_gemm_stream(false, p.fp8, false, g2, p.tile_rows, p.max_light, cus, st));
     else FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.wk2, p.max_light, cus, st));
+    record(ev, FMOE_STAGE_GEMM2_HEAVY, st);
     if (heavy_possible) {
         GemmArgs g2h = g2;
         g2h.mtiles = mtiles_heavy;

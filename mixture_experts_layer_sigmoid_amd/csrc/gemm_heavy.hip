@@ -98,7 +98,7 @@ constexpr int weight_wait() {
 
 template <bool GATED, bool FP8>
 constexpr int ring_depth() {
-    return FP8 ? (GATED ? 2 : 4) : (GATED ? 8 : 8);
+    return FP8 ? (GATED ? 2 : 4) : (GATED ? 4 : 8);
 }
 
 template <bool GATED, bool FP8, bool OUT_F32>
@@ -202,37 +202,62 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
 #pragma unroll
                 for (int h = 0; h < NW; h++) acc[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            // step s of the chunk in buffer B, weights from ring slot `slot`
+            // step s of the chunk in buffer B, weights from ring slot `slot`.  The activation
+            // fragments are read in groups of GS sub-blocks, double-buffered, so the reads of
+            // the next group are in flight while the current group's MFMAs run.
+            constexpr int GS = NS < 4 ? NS : 4;
+            constexpr int NG = NS / GS;
             auto compute = [&](auto Bc, int slot, int s, int step) {
                 constexpr int B = decltype(Bc)::value;
                 const i32x4* X = B == 0 ? X0 : B == 1 ? X1 : B == 2 ? X2 : X3;
+                i32x4 xr[2][GS][C::HALVES];
+                auto read_group = [&](auto Gc) {
+                    constexpr int G = decltype(Gc)::value;
 #pragma unroll
-                for (int sb = 0; sb < NS; sb++) {
-                    if constexpr (!FP8) {
-                        const bf16x8 xb = __builtin_bit_cast(bf16x8, X[(s * NS + sb) * 64 + lane]);
+                    for (int q = 0; q < GS; q++)
 #pragma unroll
-                        for (int h = 0; h < NW; h++)
-                            acc[sb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[slot][h], xb, acc[sb][h], 0, 0, 0);
-                    } else {
-                        const float* A = B == 0 ? A0 : B == 1 ? A1 : B == 2 ? A2 : A3;
-                        const i32x4 lo = X[(sb * 2) * 64 + lane];
-                        const i32x4 hi = X[(sb * 2 + 1) * 64 + lane];
-                        const i32x8 xb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        const float sa = A[sb * 16 + r16];
-                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                        for (int hf = 0; hf < C::HALVES; hf++)
+                            xr[G & 1][q][hf] = X[((s * NS + G * GS + q) * C::HALVES + hf) * 64 + lane];
+                };
+                auto mfma_group = [&](auto Gc) {
+                    constexpr int G = decltype(Gc)::value;
 #pragma unroll
-                        for (int h = 0; h < NW; h++) {
-                            const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw[slot][h], xb, zero,
-                                                                                               0, 0, 0, 0, 0, 0);
-                            const float cs = WS[h][step] * sa;
+                    for (int q = 0; q < GS; q++) {
+                        const int sb = G * GS + q;
+                        if constexpr (!FP8) {
+                            const bf16x8 xb = __builtin_bit_cast(bf16x8, xr[G & 1][q][0]);
 #pragma unroll
-                            for (int i = 0; i < 4; i++) acc[sb][h][i] = __builtin_fmaf(pr[i], cs, acc[sb][h][i]);
+                            for (int h = 0; h < NW; h++)
+                                acc[sb][h] =
+                                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[slot][h], xb, acc[sb][h], 0, 0, 0);
+                        } else {
+                            const float* A = B == 0 ? A0 : B == 1 ? A1 : B == 2 ? A2 : A3;
+                            const i32x4 lo = xr[G & 1][q][0], hi = xr[G & 1][q][C::HALVES - 1];
+                            const i32x8 xb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            const float sa = A[sb * 16 + r16];
+                            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int h = 0; h < NW; h++) {
+                                const f32x4 pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    bw[slot][h], xb, zero, 0, 0, 0, 0, 0, 0);
+                                const float cs = WS[h][step] * sa;
+#pragma unroll
+                                for (int i = 0; i < 4; i++) acc[sb][h][i] = __builtin_fmaf(pr[i], cs, acc[sb][h][i]);
+                            }
                         }
                     }
-                    // interleave: one fragment read ahead of the matrix operations that use it
-                    __builtin_amdgcn_sched_group_barrier(0x100, C::HALVES, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, NW, 0);
-                }
+                };
+                read_group(std::integral_constant<int, 0>{});
+                __builtin_amdgcn_sched_group_barrier(0x100, GS * C::HALVES, 0);
+                static_for<0, NG>([&](auto Gc) {
+                    constexpr int G = decltype(Gc)::value;
+                    if constexpr (G + 1 < NG) {
+                        read_group(std::integral_constant<int, G + 1>{});
+                        __builtin_amdgcn_sched_group_barrier(0x100, GS * C::HALVES, 0);
+                    }
+                    mfma_group(Gc);
+                    __builtin_amdgcn_sched_group_barrier(0x008, GS * NW, 0);
+                });
             };
 
             // prologue: chunks 0..2 in flight, D weight steps in flight, chunk 0 landed

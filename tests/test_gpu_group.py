@@ -43,6 +43,7 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
 @pytest.mark.parametrize("T,k,E,ep_size,ep_rank", [
     (1, 1, 1, 1, 0), (1, 8, 128, 1, 0), (37, 3, 16, 1, 0), (64, 8, 128, 1, 0), (300, 4, 8, 1, 0),
     (288, 6, 400, 8, 0), (288, 6, 400, 8, 5), (513, 8, 64, 4, 3), (4096, 8, 128, 1, 0), (2000, 2, 1024, 1, 0),
+    (512, 8, 128, 1, 0), (1024, 4, 16, 1, 0), (1040, 4, 16, 2, 1),  # 64 chunks (one launch), 65 chunks
 ])
 def test_group_random_ids_with_duplicates(T, k, E, ep_size, ep_rank):
     announce(f"group T={T} k={k} E={E} ep={ep_size}/{ep_rank}")
