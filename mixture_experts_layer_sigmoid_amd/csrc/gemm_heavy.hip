@@ -115,6 +115,7 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
     __shared__ i32x4 X0[kHvFrags * 64], X1[kHvFrags * 64], X2[kHvFrags * 64], X3[kHvFrags * 64];
     __shared__ float A0[FP8 ? 256 : 1], A1[FP8 ? 256 : 1], A2[FP8 ? 256 : 1], A3[FP8 ? 256 : 1];
     __shared__ float WS[2][FP8 ? kMaxKBlocks : 1];
+    __shared__ int split_last;  // this workgroup completed a split task's reduction
 
     const int lane = lane_id();
     const int v = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -125,10 +126,27 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
     const int nch = (nsteps + CS - 1) / CS;
     const size_t rowbytes = (size_t)K * C::EB;
     const int nblocks = g.N / kHvFeatures;
-    const int total = *g.tile_count * nblocks;
+    const int tasks = *g.tile_count * nblocks;
     const int topk = g.perm_src ? g.topk : 1;
+    // Too few tasks for the GPU (a few hot experts): split each task's reduction over KS
+    // workgroups, whole groups of four chunks each; every split leaves its fp32 partial in its
+    // own slot and the last to finish adds them in split order (a fixed order, so the result does
+    // not depend on which one is last) and writes the output.  The partials of a task (written
+    // and read back: 2 KS rows 4 bytes per feature) stay within a quarter of its weight bytes
+    // (K per feature, times the element size), with rows those of the largest tile.
+    const int ngroups = ((nsteps + CS - 1) / CS + 3) / 4;
+    const int slots = min((int)gridDim.x, kSplitSlots);
+    int KS = 1;
+    if (g.part != nullptr && tasks > 0 && 2 * tasks <= slots) {
+        const int big = max(16, min(*g.max_rows, heavy_max_rows(FP8)));
+        const int by_bytes = (int)(rowbytes / (32 * (size_t)big));
+        KS = max(1, min(min(min(8, slots / tasks), ngroups), by_bytes));
+    }
+    const int total = tasks * KS;
 
-    for (int task = blockIdx.x; task < total; task += gridDim.x) {
+    for (int tl = blockIdx.x; tl < total; tl += gridDim.x) {
+        const int task = tl / KS;
+        const int ks = tl - task * KS;
         const int mt = task / nblocks;
         const int nb = task - mt * nblocks;
         // the tile list is read-only here: a scalar load through the constant address space
@@ -143,6 +161,8 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
             constexpr int QD = QX + (FP8 ? 1 : 0);       // with the activation-scale load
             constexpr int NWAIT = cap63(2 * QD + cmin(2 * CS, D + CS) * WL);
             constexpr int NPRO = cap63(2 * QD + D * WL);
+            // this split's chunks [cb, ce): whole groups of four
+            const int cb = 4 * (ks * ngroups / KS), ce = 4 * ((ks + 1) * ngroups / KS);
 
             // staging sources: wavefront v loads pieces (v*QX + j) mod F; piece f is step
             // f / (NS HALVES) of the chunk, sub-block (f / HALVES) % NS, half f % HALVES (waves
@@ -262,14 +282,14 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
 
             // prologue: chunks 0..2 in flight, D weight steps in flight, chunk 0 landed
             __builtin_amdgcn_sched_barrier(0);
-            stage(std::integral_constant<int, 0>{}, 0);
+            stage(std::integral_constant<int, 0>{}, cb);
             __builtin_amdgcn_sched_barrier(0);
-            stage(std::integral_constant<int, 1>{}, 1);
+            stage(std::integral_constant<int, 1>{}, cb + 1);
             __builtin_amdgcn_sched_barrier(0);
-            stage(std::integral_constant<int, 2>{}, 2);
+            stage(std::integral_constant<int, 2>{}, cb + 2);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int d = 0; d < D; d++) issue_w(d, d);
+            for (int d = 0; d < D; d++) issue_w(d, cb * CS + d);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<NPRO>();
             compiler_fence();
@@ -304,22 +324,19 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
             // whole groups of four chunks (an early exit would cost the exact wait counts the
             // compiler keeps across the loop); chunks past the end load clamped addresses and
             // compute nothing
-            for (int c0 = 0; c0 < nch; c0 += 4) {
+            for (int c0 = cb; c0 < ce; c0 += 4) {
                 chunk(std::integral_constant<int, 0>{}, c0);
                 chunk(std::integral_constant<int, 1>{}, c0 + 1);
                 chunk(std::integral_constant<int, 2>{}, c0 + 2);
                 chunk(std::integral_constant<int, 3>{}, c0 + 3);
             }
 
-            // epilogue: lane holds tile row sb*16 + r16 and features nb*128 + v*16 + kg*4 + i
-#pragma unroll
-            for (int sb = 0; sb < NS; sb++) {
-                const int col = sb * 16 + r16;
-                if (col >= rows) continue;
+            // output of tile row col (this lane's sub-block row), features nb*128 + v*16 + kg*4 + i
+            auto store = [&](int col, const f32x4& a0, const f32x4& a1) {
                 const size_t o = (size_t)(row0 + col) * g.N + nb * kHvFeatures + v * 16 + kg * 4;
                 float r[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_h(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
+                for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_h(a0[i], a1[i]) : a0[i];
                 if (OUT_F32) {
                     *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
                 } else {
@@ -328,6 +345,64 @@ __global__ __launch_bounds__(kHvThreads) void k_grouped_gemm_heavy(GemmArgs g) {
                     pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
                     *(uint2*)((uint16_t*)g.out + o) = pk;
                 }
+            };
+
+            if (KS == 1) {
+                // epilogue: lane holds tile rows sb*16 + r16
+#pragma unroll
+                for (int sb = 0; sb < NS; sb++) {
+                    const int col = sb * 16 + r16;
+                    if (col < rows) store(col, acc[sb][0], acc[sb][NW - 1]);
+                }
+                return;
+            }
+            // split reduction: every split leaves its partial in its slot (slot tl holds
+            // [2][part_rows][128] fp32), the last to arrive adds the KS partials in split order.
+            // The partials move through device-scope (sc1) 16-byte buffer stores and loads, which
+            // write through / bypass the per-XCD L2; a device-wide fence instead would write
+            // back and invalidate the whole L2 under every other workgroup's weight stream.
+            // Each lane's stores are acknowledged (vmcnt 0) before the workgroup barrier and the
+            // arrival count, and the last workgroup reads only after it has counted every
+            // arrival.  Offsets past the buffer are dropped by the hardware range check.
+            const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+                g.part, (short)0, (int)((size_t)kSplitSlots * 2 * g.part_rows * kHvFeatures * 4), 0x00020000);
+            auto slot_off = [&](int slot, int h, int col) {
+                return (int)(((((size_t)slot * 2 + h) * g.part_rows + col) * kHvFeatures + v * 16 + kg * 4) * 4);
+            };
+            constexpr int kDeviceScope = 16;  // cache policy: sc1
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++) {
+                const int col = sb * 16 + r16;
+                if (col >= rows) continue;
+#pragma unroll
+                for (int h = 0; h < NW; h++)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[sb][h]), prs,
+                                                           slot_off(tl, h, col), 0, kDeviceScope);
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int before = __hip_atomic_fetch_add(&g.sem[task], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                split_last = before == KS - 1;
+                // ready for the next launch (kernel boundaries order it before any later use)
+                if (before == KS - 1)
+                    __hip_atomic_store(&g.sem[task], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            if (!split_last) return;
+            for (int sb = 0; sb < NS; sb++) {
+                const int col = sb * 16 + r16;
+                if (col >= rows) continue;
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < KS; j++) {
+                    s0 += __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, slot_off(task * KS + j, 0, col), 0, kDeviceScope));
+                    if constexpr (GATED)
+                        s1 += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            prs, slot_off(task * KS + j, 1, col), 0, kDeviceScope));
+                }
+                store(col, s0, s1);
             }
         };
 
@@ -367,6 +442,8 @@ hipError_t launch_heavy(const GemmArgs& a, int max_tiles, int cus, hipStream_t s
     long long grid = (long long)max_tiles * (a.N / kHvFeatures);
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
+    // with partial-sum slots, enough workgroups to split the reductions of a few tiles
+    if (a.part != nullptr && grid < (cap < kSplitSlots ? cap : kSplitSlots)) grid = cap < kSplitSlots ? cap : kSplitSlots;
     if (grid < 1) grid = 1;
     k_grouped_gemm_heavy<GATED, FP8, OUT_F32><<<(unsigned)grid, kHvThreads, 0, st>>>(a);
     return hipGetLastError();

@@ -2,14 +2,14 @@
 // GEMMs.
 //
 // The flat assignments i = t*k + j are cut into chunks of 64, one wavefront each.  Inside a
-// chunk the lanes that hold the same local expert find each other with wavefront ballots,
-// so each assignment gets its rank among the earlier assignments of its expert in the chunk
-// and each (chunk, expert) its count, without atomics.  A scan per expert over the chunks
+// chunk the lanes that hold the same local expert find each other with one wavefront ballot
+// per bit of the local expert index, so each assignment gets its rank among the earlier
+// assignments of its expert in the chunk and each (chunk, expert) its count, without atomics.  A scan per expert over the chunks
 // and a scan over the experts then give every (chunk, expert) its first grouped row, and a
 // last pass writes every assignment to base + rank.  The result is the stable counting sort
 // (experts ascending, flat index ascending inside an expert), identical on every run.
 //
-// Small batches (at most 16 chunks) run all three phases in one workgroup and one launch;
+// Small batches (at most 64 chunks) run all three phases in one workgroup and one launch;
 // larger ones run a counting launch over all chunks, a one-workgroup scan, and a scatter
 // launch, so the ballot work spreads over the whole GPU.
 //
@@ -24,7 +24,8 @@
 namespace fmoe {
 
 constexpr int kScanThreads = 1024;
-constexpr int kSmallChunks = 16;  // chunks (wavefronts) of the one-workgroup path
+constexpr int kSmallChunks = 64;  // chunks of the one-workgroup path
+constexpr int kSmallPerWave = kSmallChunks / (kScanThreads / 64);  // chunks per wavefront there
 constexpr int kScanShared = 32 + 1536;  // LDS ints of scan_and_tile
 
 // Phase 1 for one chunk of 64 assignments, by one wavefront.  Writes the chunk's count of
@@ -44,15 +45,20 @@ __device__ void chunk_rank(const int32_t* __restrict__ ids, int n, int E, int El
         else if (id - lo >= 0 && id - lo < El) l = id - lo;
     }
     *bad = __popcll(__ballot(b));
-    unsigned long long pending = __ballot(l >= 0);
+    // lanes with the same local expert: those that agree with this lane on every bit of l (one
+    // ballot per bit of El - 1), among the lanes holding a local expert
+    const unsigned long long live = __ballot(l >= 0);
+    unsigned long long same = live;
+    const int nbits = El > 1 ? 32 - __clz(El - 1) : 0;
+    for (int bit = 0; bit < nbits; bit++) {
+        const bool set = (l >> bit) & 1;
+        const unsigned long long m = __ballot(set);
+        same &= set ? m : ~m;
+    }
     int r = -1;
-    while (pending) {
-        const int leader = __ffsll((long long)pending) - 1;
-        const int lv = __shfl(l, leader, 64);
-        const unsigned long long m = __ballot(l == lv);
-        if (l == lv) r = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == leader) mask[lv] = __popcll(m);
-        pending &= ~m;
+    if (l >= 0) {
+        r = __popcll(same & ((1ull << lane) - 1ull));
+        if (r == 0) mask[l] = __popcll(same);  // the first lane of each expert writes its count
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -107,7 +113,7 @@ __device__ int block_max(int v, int* sh) {
 // (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
 // threads read consecutive experts of a chunk.
 __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int heavy_rows, int rows_estimate,
-                              long long dropped,
+                              long long dropped, int* __restrict__ sem,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
                               int* sh /* >= kScanShared ints */) {
@@ -207,6 +213,9 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
             }
         }
     }
+    // arrival counts of the heavy GEMMs' split reductions start at zero for this call
+    if (sem != nullptr)
+        for (int q = threadIdx.x; q < kSplitSlots; q += kScanThreads) sem[q] = 0;
     if (threadIdx.x == 0) {
         offsets[El] = R;
         hdr->m_tiles = n_light;
@@ -238,27 +247,42 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
                                                              int lo, int tile_rows, int heavy_rows, int rows_estimate,
-                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                             int* __restrict__ sem, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
                                                              int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                                              MTile* __restrict__ mtiles_heavy,
                                                              DevHeader* __restrict__ hdr) {
     extern __shared__ int lds[];
     const int nchunk = (n + 63) / 64;  // <= kSmallChunks
+    constexpr int NW = kScanThreads / 64;
     int* cnt = lds;                        // [nchunk][El]
-    int* mask = cnt + El * nchunk;         // [nchunk][El]
-    int* bads = mask + nchunk * El;        // [kSmallChunks]
+    int* mask = cnt + El * nchunk;         // [NW][El]
+    int* bads = mask + NW * El;            // [kSmallChunks]
     int* sh = bads + kSmallChunks;         // scan scratch [kScanShared]
     const int w = threadIdx.x >> 6;
-    int l = -1, r = -1, bad = 0;
-    if (w < nchunk) chunk_rank(ids, n, E, El, lo, w, cnt + w * El, 1, mask + w * El, &l, &r, &bad);
-    if (w < nchunk && lane_id() == 0) bads[w] = bad;
+    // wavefront w ranks chunks w, w + NW, ...
+    int l[kSmallPerWave], r[kSmallPerWave];
+#pragma unroll
+    for (int j = 0; j < kSmallPerWave; j++) {
+        const int c = w + j * NW;
+        l[j] = r[j] = -1;
+        if (c < nchunk) {
+            int bad = 0;
+            chunk_rank(ids, n, E, El, lo, c, cnt + c * El, 1, mask + w * El, &l[j], &r[j], &bad);
+            if (lane_id() == 0) bads[c] = bad;
+        }
+    }
     __syncthreads();
     long long dropped = 0;
     for (int c = 0; c < nchunk; c++) dropped += bads[c];
-    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, sem, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
     __syncthreads();
-    if (w < nchunk) chunk_scatter(w * 64 + lane_id(), n, l, r, l >= 0 ? cnt[w * El + l] : 0, perm_src, inv_perm);
+#pragma unroll
+    for (int j = 0; j < kSmallPerWave; j++) {
+        const int c = w + j * NW;
+        if (c < nchunk)
+            chunk_scatter(c * 64 + lane_id(), n, l[j], r[j], l[j] >= 0 ? cnt[c * El + l[j]] : 0, perm_src, inv_perm);
+    }
 }
 
 // ---------------------------------------------------------------- multi-workgroup path
@@ -280,7 +304,7 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int heavy_rows, int rows_estimate,
+                                                            int heavy_rows, int rows_estimate, int* __restrict__ sem,
                                                             const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
@@ -295,7 +319,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, sem, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
 }
 
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
@@ -315,13 +339,13 @@ size_t group_scratch_bytes(long long n, int El) {
 }
 
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
-                        int rows_estimate,
+                        int rows_estimate, int* sem,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
-    const size_t lds = (size_t)(2 * El * nchunk + kSmallChunks + kScanShared) * 4;
+    const size_t lds = (size_t)(El * nchunk + (kScanThreads / 64) * El + kSmallChunks + kScanShared) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
-        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts,
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, sem, counts,
                                                     offsets,
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
         return hipGetLastError();
@@ -329,7 +353,7 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
     int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, bad, counts,
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, sem, bad, counts,
                                              offsets, mtiles,
                                              mtiles_heavy, hdr);
     k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);

@@ -155,3 +155,25 @@ def test_forward_is_deterministic_and_matches_experts():
         assert torch.equal(again, first)
     out2 = fm.fmoe_experts(L.shape, L.x_gpu, ids, wts, L.w)
     assert torch.equal(out2, first)
+
+
+def test_profiled_forward_and_hip_graph_replays_match_eager():
+    announce("profiled forward and HIP graph capture/replays vs eager (concentrated, heavy tiles)")
+    L = Layer(config=synth.BF16_LAYER, T=256, H=2048, I=768, E=128, k=8, routing="concentrated")
+    ws = fm.workspace(L.shape)
+    eager = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws)
+    assert fm.fmoe_read_stats(ws)["heavy_tiles"] > 0
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(fm.FMOE_NUM_STAGES + 1)]
+    profiled = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, stage_events=evs)
+    assert torch.equal(profiled, eager)
+    out = torch.empty_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, out=out)
+    for i in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        # eager work between the replays
+        assert torch.equal(fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws), eager)
