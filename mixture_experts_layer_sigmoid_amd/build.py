@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfmoe.so")
-SOURCES = ["router.hip", "group.hip", "quant.hip", "gemm.hip", "gemm_stream.hip", "gemm_heavy.hip", "combine.hip", "abi.cpp"]
+SOURCES = ["router.hip", "group.hip", "quant.hip", "gemm.hip", "gemm_stream.hip", "gemm_tiled.hip", "combine.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 
@@ -34,7 +34,7 @@ def flags() -> list[str]:
 # per-source extra flags: the heavy kernel keeps MFMA accumulators in ordinary VGPRs (its
 # register budget at two wavefronts per SIMD holds them, and the accumulator-register form
 # makes the compiler copy them between register files every loop iteration)
-EXTRA_FLAGS = {"gemm_heavy.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"gemm_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build(verbose: bool = False) -> str:

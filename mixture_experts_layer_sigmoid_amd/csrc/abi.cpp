@@ -31,7 +31,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Worst-case workspace layout of one call.
 struct Layout {
-    size_t hdr, ids, wts, counts, offsets, perm, inv, rank, grp, mtiles, sem, part, xq, xs, h, hq, hs, y, total;
+    size_t hdr, ids, wts, counts, offsets, perm, inv, rank, grp, mtiles, xq, xs, h, hq, hs, y, total;
 };
 
 struct Plan {
@@ -43,7 +43,6 @@ struct Plan {
     int heavy_rows;      // rows of a full heavy tile
     int max_light;       // bounds on light and heavy row tiles for any routing
     int max_heavy;
-    int part_rows;       // rows of one partial-sum slot of a split heavy reduction (0: no heavy tiles possible)
     int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
     Layout L;
 };
@@ -122,11 +121,6 @@ Plan make_plan(const fmoe_shape* s) {
     L.rank = take(n * 4);
     L.grp = take(group_scratch_bytes((long long)n, p.El));
     L.mtiles = take((size_t)(p.max_light + p.max_heavy) * sizeof(MTile));
-    // heavy tiles exist only if some expert can hold more than tile_rows rows; a split heavy
-    // reduction keeps one fp32 partial per workgroup slot: 2 matrices x (tile rows) x 128 features
-    p.part_rows = p.n > p.tile_rows ? (int)((p.n < p.heavy_rows ? (p.n + 15) / 16 * 16 : p.heavy_rows)) : 0;
-    L.sem = take((size_t)kSplitSlots * 4);
-    L.part = take((size_t)kSplitSlots * 2 * p.part_rows * 128 * 4);
     if (p.fp8) {
         L.xq = take((size_t)p.T * p.H);
         L.xs = take((size_t)p.T * (p.H / 128) * 4);
@@ -190,7 +184,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     record(ev, FMOE_STAGE_GROUP, st);
     MTile* mtiles_heavy = mtiles + p.max_light;
     FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.heavy_rows, p.rows_estimate,
-                          (int*)(ws + L.sem), (int32_t*)(ws + L.counts),
+                          (int32_t*)(ws + L.counts),
                           (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
                           mtiles_heavy, hdr, st));
     // an expert can hold more than tile_rows rows only if more assignments than that can name it
@@ -214,21 +208,13 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g1.out = ws + L.h;
     g1.mtiles = mtiles;
     g1.tile_count = &hdr->m_tiles;
-    g1.part = nullptr;
-    g1.sem = nullptr;
-    g1.part_rows = 0;
-    g1.max_rows = nullptr;
     GemmArgs g1h = g1;
     g1h.mtiles = mtiles_heavy;
     g1h.tile_count = &hdr->m_tiles_heavy;
-    g1h.part = (float*)(ws + L.part);
-    g1h.sem = (int*)(ws + L.sem);
-    g1h.part_rows = p.part_rows;
-    g1h.max_rows = &hdr->max_rows;
     if (p.wk1 == 1) FMOE_TRY(launch_grouped_gemm_stream(true, p.fp8, p.fp8, g1, p.tile_rows, p.max_light, cus, st));
     else FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_light, cus, st));
     record(ev, FMOE_STAGE_GEMM1_HEAVY, st);
-    if (heavy_possible) FMOE_TRY(launch_grouped_gemm_heavy(true, p.fp8, p.fp8, g1h, p.max_heavy, cus, st));
+    if (heavy_possible) FMOE_TRY(launch_grouped_gemm_tiled(true, p.fp8, p.fp8, g1h, p.max_heavy, cus, st));
 
     record(ev, FMOE_STAGE_QUANT_H, st);
     if (p.fp8)
@@ -249,21 +235,13 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     g2.out = ws + L.y;
     g2.mtiles = mtiles;
     g2.tile_count = &hdr->m_tiles;
-    g2.part = nullptr;
-    g2.sem = nullptr;
-    g2.part_rows = 0;
-    g2.max_rows = nullptr;
     GemmArgs g2h = g2;
     g2h.mtiles = mtiles_heavy;
     g2h.tile_count = &hdr->m_tiles_heavy;
-    g2h.part = (float*)(ws + L.part);
-    g2h.sem = (int*)(ws + L.sem);
-    g2h.part_rows = p.part_rows;
-    g2h.max_rows = &hdr->max_rows;
     if (p.wk2 == 1) FMOE_TRY(launch_grouped_gemm_stream(false, p.fp8, false, g2, p.tile_rows, p.max_light, cus, st));
     else FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g2, p.tile_rows, p.wk2, p.max_light, cus, st));
     record(ev, FMOE_STAGE_GEMM2_HEAVY, st);
-    if (heavy_possible) FMOE_TRY(launch_grouped_gemm_heavy(false, p.fp8, false, g2h, p.max_heavy, cus, st));
+    if (heavy_possible) FMOE_TRY(launch_grouped_gemm_tiled(false, p.fp8, false, g2h, p.max_heavy, cus, st));
 
     record(ev, FMOE_STAGE_COMBINE, st);
     FMOE_TRY(launch_combine(ws + L.y, inv, wts, p.T, p.k, p.H, out, st));
@@ -351,7 +329,7 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
     char* wsb = (char*)ws;
     MTile* mt = (MTile*)(wsb + p.L.mtiles);
     return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.heavy_rows, p.rows_estimate,
-                                   (int*)(wsb + p.L.sem), counts, offsets,
+                                   counts, offsets,
                                    perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp), mt,
                                    mt + p.max_light, (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
 }

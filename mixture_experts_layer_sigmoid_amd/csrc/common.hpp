@@ -14,11 +14,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr float kE4M3Max = 448.0f;  // largest finite OCP E4M3FN magnitude
 constexpr int kMaxKBlocks = 512;    // 128-deep blocks of the reduction dimension (65536 / 128)
 constexpr int kLightRows = 32;      // largest row tile of the light GEMM kernel
-// largest row tile of the heavy GEMM kernel: 256 rows (16 sub-blocks of 16) with bf16 weights;
-// 128 with FP8, whose larger operand fragments leave registers for 8 sub-blocks
-constexpr int heavy_max_rows(bool fp8) { return fp8 ? 128 : 256; }
-constexpr int kHeavyRowsMax = 256;
-constexpr int kSplitSlots = 256;    // workgroups of a heavy GEMM that may split a reduction (partial-sum slots)
+// largest row tile of the heavy GEMM kernel (4 groups of 64 rows)
+constexpr int heavy_max_rows(bool) { return 256; }
 
 // Workspace header written by the grouping kernel and read by later kernels and by
 // fmoe_read_stats.  Field order is part of the workspace format of this library only.

@@ -8,7 +8,7 @@
 // is fused into the operand load), or row p itself when no map is given.
 //
 // This light kernel takes row tiles of at most 32 rows (experts with few rows); heavier
-// experts go to gemm_heavy.hip.
+// experts go to gemm_tiled.hip.
 //
 // Shape of the work: weights are the bytes that matter (at decode every weight byte is used
 // by a handful of rows), so each wavefront streams its own 16 weight rows straight from HBM

@@ -1,0 +1,310 @@
+// gemm_tiled.hip -- grouped expert GEMMs for heavy row tiles, both operands tiled through LDS.
+//
+// Same operation as gemm.hip (gate/up with SiLU-and-mul, or down; bf16 or FP8 block-scaled),
+// for experts that hold more rows than a light tile: large batches, and the hot experts of a
+// concentrated routing ("vLLM Community Traces H20 MoE Scheduling Inefficiency to
+// Expert-Load Kernel Selection", paragraph 4: concentrated routing needs another kernel choice
+// than the average).  With up to 256 rows per tile the work is a dense contraction, so the
+// kernel is built around the matrix cores rather than the weight stream.
+//
+// Shape: one workgroup of 8 wavefronts computes a tile of up to 256 rows times 128 weight
+// columns (gate/up: 64 features of each matrix, so SiLU-and-mul happens in registers); the
+// wavefronts form a 4 x 2 grid, each owning 64 rows x 64 columns (16 accumulators of 16 x 16).
+// Every 128-byte slice of the reduction (64 bf16 or 128 e4m3 per row) is one stage: the
+// activation rows (gathered through the row map) and the weight rows are copied straight from
+// global memory into LDS by direct global-to-LDS loads, three stages deep, so two stages are in
+// flight while one is read.  A stage row of 8 pieces of 16 bytes keeps piece c at position
+// c ^ ((row >> 1) & 7): the 16 rows read by one MFMA fragment then fall in 16 different bank
+// groups.  Each buffer is a separate LDS array and every wait is an explicit count of the loads
+// that must have landed, so the compiler never has to wait for loads into another buffer.
+//
+// Per stage and wavefront: 8 fragment reads (16 KB) feed 32 MFMAs of 16x16x32 (bf16), or
+// 4 + 4 double-width reads feed 16 MFMAs of 16x16x128 (FP8, one per 128-deep scale block,
+// whose product is added times weight scale x activation scale).
+//
+// Work order: tasks (row tile, column block) run column block fastest, and the persistent
+// workgroups of one XCD (workgroup ids equal mod 8) take consecutive tasks, so the tasks that
+// share a tile's activations or an expert's weights run at the same time behind one L2.
+#include <type_traits>
+
+#include "launch.hpp"
+
+namespace fmoe {
+
+namespace {
+
+constexpr int kTgRows = 256;     // rows of a tile at most
+constexpr int kTgCols = 128;     // weight columns per workgroup
+constexpr int kTgThreads = 512;  // 8 wavefronts
+constexpr int kTgXPieces = kTgRows * 8;  // 16-byte pieces of one activation stage
+constexpr int kTgWPieces = kTgCols * 8;  // 16-byte pieces of one weight stage
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+template <int N>
+__device__ __forceinline__ void tg_wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void tg_fence() { asm volatile("" ::: "memory"); }
+// workgroup barrier without the full memory wait __syncthreads implies around LDS DMA
+__device__ __forceinline__ void tg_barrier() {
+    tg_fence();
+    __builtin_amdgcn_s_barrier();
+    tg_fence();
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void tg_static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        tg_static_for<I + 1, N>(f);
+    }
+}
+
+__device__ __forceinline__ float tg_silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// position of piece c of stage row r
+__device__ __forceinline__ int tg_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+template <bool GATED, bool FP8, bool OUT_F32>
+__global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
+    __shared__ i32x4 X0[kTgXPieces], X1[kTgXPieces], X2[kTgXPieces];
+    __shared__ i32x4 W0[kTgWPieces], W1[kTgWPieces], W2[kTgWPieces];
+    __shared__ float SA0[FP8 ? kTgRows : 1], SA1[FP8 ? kTgRows : 1], SA2[FP8 ? kTgRows : 1];
+
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 1, wn = w & 1;  // row group (64 rows) and column group (64 columns)
+    const int r16 = lane & 15, kg = lane >> 4;
+    const int K = g.K;
+    const size_t rowbytes = (size_t)K * (FP8 ? 1 : 2);
+    const int nkb = K / (FP8 ? 128 : 64);  // stages
+    const int nkb128 = K >> 7;             // 128-deep scale blocks
+    const int feat_per_task = GATED ? kTgCols / 2 : kTgCols;
+    const int nblocks = g.N / feat_per_task;
+    const int tasks = *g.tile_count * nblocks;
+    const int topk = g.perm_src ? g.topk : 1;
+
+    // workgroups of one XCD (ids equal mod 8) take consecutive tasks
+    const int G = gridDim.x;
+    const int li = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+
+    // fragment read offset of this lane inside a 16-row block, for piece group q (0..1)
+    int frag[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) frag[q] = tg_slot(r16, q * 4 + kg);
+
+    for (int t = li; t < tasks; t += G) {
+        const int mt = t / nblocks;
+        const int nb = t - mt * nblocks;
+        // the tile list is read-only here: a scalar load through the constant address space
+        const i32x4 mv = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + mt);
+        const int expert = mv[0], row0 = mv[1], rows = mv[2];
+        // every load of the previous task has landed and every wavefront is past its last
+        // stage, so all buffers are free
+        tg_wait_vmcnt<0>();
+        __syncthreads();
+
+        auto run = [&](auto NAc) {
+            constexpr int NA = decltype(NAc)::value;  // activation loads per stage = 64-row groups
+            constexpr int L = NA + 2 + (FP8 ? 1 : 0);  // vector-memory instructions per stage
+            // activation pieces: load j of wavefront w covers stage rows (j*8 + w)*8 .. +8
+            size_t xoff[NA];
+#pragma unroll
+            for (int j = 0; j < NA; j++) {
+                const int r = (j * 8 + w) * 8 + (lane >> 3);
+                const int p = row0 + min(r, rows - 1);
+                const int src = (g.perm_src ? g.perm_src[p] : p) / topk;
+                const int c = (lane & 7) ^ ((r >> 1) & 7);
+                xoff[j] = (size_t)src * rowbytes + c * 16;
+            }
+            // weight pieces: load j covers weight columns (j*8 + w)*8 .. +8 of the block
+            const uint8_t* wsrc[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int q = (j * 8 + w) * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ ((q >> 1) & 7);
+                const uint8_t* base;
+                size_t wrow;
+                if constexpr (GATED) {
+                    base = (const uint8_t*)(q < 64 ? g.W0 : g.W1);
+                    wrow = (size_t)expert * g.N + nb * 64 + (q & 63);
+                } else {
+                    base = (const uint8_t*)g.W0;
+                    wrow = (size_t)expert * g.N + nb * kTgCols + q;
+                }
+                wsrc[j] = base + wrow * rowbytes + c * 16;
+            }
+            // FP8 activation scales: wavefront w stages the scales of rows (w & 3)*64 + lane
+            int ssrc = 0;
+            if constexpr (FP8) {
+                const int r = (w & 3) * 64 + lane;
+                const int p = row0 + min(r, rows - 1);
+                ssrc = (g.perm_src ? g.perm_src[p] : p) / topk;
+            }
+
+            auto issue = [&](auto Bc, int kb) {
+                constexpr int B = decltype(Bc)::value;
+                i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
+                i32x4* W = B == 0 ? W0 : B == 1 ? W1 : W2;
+                const size_t ko = (size_t)kb * 128;
+#pragma unroll
+                for (int j = 0; j < NA; j++)
+                    __builtin_amdgcn_global_load_lds((gbl_void*)((const uint8_t*)g.A + xoff[j] + ko),
+                                                     (lds_void*)(X + (j * 8 + w) * 64), 16, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    __builtin_amdgcn_global_load_lds((gbl_void*)(wsrc[j] + ko), (lds_void*)(W + (j * 8 + w) * 64), 16,
+                                                     0, 0);
+                if constexpr (FP8) {
+                    float* S = B == 0 ? SA0 : B == 1 ? SA1 : SA2;
+                    __builtin_amdgcn_global_load_lds((gbl_void*)(g.A_scale + (size_t)ssrc * nkb128 + kb),
+                                                     (lds_void*)(S + (w & 3) * 64), 4, 0, 0);
+                }
+            };
+
+            f32x4 acc[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int c = 0; c < 4; c++) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            // weight rows of column block c of this wavefront (gate/up: c = 0,1 gate, 2,3 up)
+            auto wcol = [&](int c) { return GATED ? (c >> 1) * 64 + wn * 32 + (c & 1) * 16 : wn * 64 + c * 16; };
+            const bool active = wm < NA;  // this wavefront's 64 rows hold some of the tile
+            // FP8 weight scales of the block: one per matrix and 128-deep block
+            const int fb = GATED ? nb / 2 : nb;
+            const size_t sidx = ((size_t)expert * (g.N / 128) + fb) * nkb128;
+
+            auto compute = [&](auto Bc, int kb) {
+                constexpr int B = decltype(Bc)::value;
+                const i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
+                const i32x4* W = B == 0 ? W0 : B == 1 ? W1 : W2;
+                if (!active) return;
+                if constexpr (!FP8) {
+#pragma unroll
+                    for (int q = 0; q < 2; q++) {
+                        bf16x8 xa[4], wb[4];
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            xa[i] = __builtin_bit_cast(bf16x8, X[(wm * 64 + i * 16) * 8 + frag[q]]);
+#pragma unroll
+                        for (int c = 0; c < 4; c++) wb[c] = __builtin_bit_cast(bf16x8, W[wcol(c) * 8 + frag[q]]);
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+#pragma unroll
+                            for (int c = 0; c < 4; c++)
+                                acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[c], xa[i], acc[i][c], 0, 0, 0);
+                    }
+                } else {
+                    const float* S = B == 0 ? SA0 : B == 1 ? SA1 : SA2;
+                    const float ws0 = *(const __attribute__((address_space(4))) float*)(g.S0 + sidx + kb);
+                    const float ws1 =
+                        GATED ? *(const __attribute__((address_space(4))) float*)(g.S1 + sidx + kb) : ws0;
+                    i32x8 xa[4], wb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const i32x4 lo = X[(wm * 64 + i * 16) * 8 + frag[0]], hi = X[(wm * 64 + i * 16) * 8 + frag[1]];
+                        xa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        const i32x4 lo = W[wcol(c) * 8 + frag[0]], hi = W[wcol(c) * 8 + frag[1]];
+                        wb[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float sa = S[wm * 64 + i * 16 + r16];
+#pragma unroll
+                        for (int c = 0; c < 4; c++) {
+                            const f32x4 pr =
+                                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[c], xa[i], zero, 0, 0, 0, 0, 0, 0);
+                            const float cs = (GATED && c >= 2 ? ws1 : ws0) * sa;
+#pragma unroll
+                            for (int e = 0; e < 4; e++) acc[i][c][e] = __builtin_fmaf(pr[e], cs, acc[i][c][e]);
+                        }
+                    }
+                }
+            };
+
+            // stage kb from buffer B: wait for it (this wavefront's loads, then everyone's),
+            // which also means every wavefront is done with stage kb-1, whose buffer then takes
+            // stage kb+2.  Every step issues its loads and waits for the same count, so the
+            // compiler's own count of the loads in flight is the same on every path: steps
+            // past the end reload the last stage (from L2) and compute nothing.
+            auto step = [&](auto Bc, int kb) {
+                constexpr int B = decltype(Bc)::value;
+                tg_wait_vmcnt<L>();
+                tg_barrier();
+                issue(std::integral_constant<int, (B + 2) % 3>{}, min(kb + 2, nkb - 1));
+                if (kb < nkb) compute(Bc, kb);
+            };
+
+            issue(std::integral_constant<int, 0>{}, 0);
+            issue(std::integral_constant<int, 1>{}, min(1, nkb - 1));
+            for (int kb = 0; kb < nkb; kb += 3) {
+                step(std::integral_constant<int, 0>{}, kb);
+                step(std::integral_constant<int, 1>{}, kb + 1);
+                step(std::integral_constant<int, 2>{}, kb + 2);
+            }
+
+            if (!active) return;
+            // lane (r16, kg) holds, for row block i and column block c, row wm*64 + 16 i + r16
+            // and the 4 columns 16 c + 4 kg .. +3 of its column group
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = wm * 64 + i * 16 + r16;
+                if (r >= rows) continue;
+#pragma unroll
+                for (int c = 0; c < (GATED ? 2 : 4); c++) {
+                    const int f = GATED ? nb * 64 + wn * 32 + c * 16 + kg * 4 : nb * kTgCols + wn * 64 + c * 16 + kg * 4;
+                    const size_t o = (size_t)(row0 + r) * g.N + f;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v[e] = GATED ? tg_silu_mul(acc[i][c][e], acc[i][c + 2][e]) : acc[i][c][e];
+                    if (OUT_F32) {
+                        *(f32x4*)((float*)g.out + o) = f32x4{v[0], v[1], v[2], v[3]};
+                    } else {
+                        uint2 pk;
+                        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                        *(uint2*)((uint16_t*)g.out + o) = pk;
+                    }
+                }
+            }
+        };
+        const int groups = (rows + 63) >> 6;
+        if (groups > 3) run(std::integral_constant<int, 4>{});
+        else if (groups > 2) run(std::integral_constant<int, 3>{});
+        else if (groups > 1) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
+    }
+}
+
+template <bool GATED, bool FP8, bool OUT_F32>
+hipError_t launch_tiled(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
+    const int per_task = GATED ? kTgCols / 2 : kTgCols;
+    long long grid = (long long)max_tiles * (a.N / per_task);
+    if (grid > cus) grid = cus;  // one workgroup per CU (the three stages take 144 KB of LDS)
+    if (grid < 1) grid = 1;
+    k_grouped_gemm_tiled<GATED, FP8, OUT_F32><<<(unsigned)grid, kTgThreads, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_tiled(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,
+                                     hipStream_t st) {
+    if (gated) {
+        if (fp8) return out_f32 ? launch_tiled<true, true, true>(a, max_tiles, cus, st)
+                                : launch_tiled<true, true, false>(a, max_tiles, cus, st);
+        return launch_tiled<true, false, false>(a, max_tiles, cus, st);
+    }
+    if (fp8) return launch_tiled<false, true, false>(a, max_tiles, cus, st);
+    return launch_tiled<false, false, false>(a, max_tiles, cus, st);
+}
+
+}  // namespace fmoe

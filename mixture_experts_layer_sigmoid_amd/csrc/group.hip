@@ -17,7 +17,7 @@
 // token count ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
 // Selection", paragraphs 3-4): an expert with 1..tile_rows rows becomes one tile of the light
 // GEMM kernel, a heavier one (a hot expert of a concentrated routing, or any expert of a large
-// batch) is cut into tiles of at most 128 rows for the heavy kernel, rows spread as evenly as
+// batch) is cut into tiles of at most 256 rows for the heavy kernel, rows spread as evenly as
 // 16-row steps allow.
 #include "launch.hpp"
 
@@ -113,7 +113,7 @@ __device__ int block_max(int v, int* sh) {
 // (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
 // threads read consecutive experts of a chunk.
 __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int heavy_rows, int rows_estimate,
-                              long long dropped, int* __restrict__ sem,
+                              long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
                               int* sh /* >= kScanShared ints */) {
@@ -146,10 +146,13 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
         total += v;
     }
     const int lead = (live && part == 0);
-    // an expert with 1..tile_rows rows is one light tile; a heavier one is cut into full heavy
-    // tiles of heavy_rows rows and one tile with the rest
+    // an expert with 1..tile_rows rows is one light tile; a heavier one is cut into
+    // ceil(total / heavy_rows) tiles of equal size rounded up to 16 rows (the last one takes
+    // the rest), so the tiles of one expert carry about the same work
     const bool heavy = total > tile_rows;
-    const int nheavy = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
+    const int nheavy0 = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
+    const int hrows = heavy ? min(heavy_rows, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
+    const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0
     int R, n_light, n_heavy, empty;
     const int first = block_scan_excl(lead ? total : 0, sh, &R);  // valid in the lead thread
     const int lfirst = block_scan_excl(lead && total > 0 && !heavy, sh, &n_light);
@@ -206,16 +209,13 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
             for (int j = part; j < nheavy; j += P) {
                 MTile mt;
                 mt.expert = e;
-                mt.row0 = my_first + j * heavy_rows;
-                mt.rows = min(heavy_rows, total - j * heavy_rows);
+                mt.row0 = my_first + j * hrows;
+                mt.rows = min(hrows, total - j * hrows);
                 mt.pad = 0;
                 mtiles_heavy[my_hfirst + j] = mt;
             }
         }
     }
-    // arrival counts of the heavy GEMMs' split reductions start at zero for this call
-    if (sem != nullptr)
-        for (int q = threadIdx.x; q < kSplitSlots; q += kScanThreads) sem[q] = 0;
     if (threadIdx.x == 0) {
         offsets[El] = R;
         hdr->m_tiles = n_light;
@@ -247,7 +247,7 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
                                                              int lo, int tile_rows, int heavy_rows, int rows_estimate,
-                                                             int* __restrict__ sem, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
                                                              int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                                              MTile* __restrict__ mtiles_heavy,
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
     __syncthreads();
     long long dropped = 0;
     for (int c = 0; c < nchunk; c++) dropped += bads[c];
-    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, sem, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kSmallPerWave; j++) {
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int heavy_rows, int rows_estimate, int* __restrict__ sem,
+                                                            int heavy_rows, int rows_estimate,
                                                             const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, sem, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
 }
 
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
@@ -339,13 +339,13 @@ size_t group_scratch_bytes(long long n, int El) {
 }
 
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
-                        int rows_estimate, int* sem,
+                        int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
     const size_t lds = (size_t)(El * nchunk + (kScanThreads / 64) * El + kSmallChunks + kScanShared) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
-        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, sem, counts,
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts,
                                                     offsets,
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
         return hipGetLastError();
@@ -353,7 +353,7 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
     int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, sem, bad, counts,
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, bad, counts,
                                              offsets, mtiles,
                                              mtiles_heavy, hdr);
     k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);

@@ -18,12 +18,6 @@ struct GemmArgs {
     void* out;                // [R, N] bf16, or fp32
     const MTile* mtiles;      // this kernel's row-tile list
     const int* tile_count;    // its length (written by the grouping kernel)
-    float* part;              // heavy kernel: fp32 partial sums of split reductions, kSplitSlots slots
-                              // of [2][part_rows][128] (nullptr: never split)
-    int* sem;                 // heavy kernel: per-task arrival counts of the splits (kSplitSlots, zeroed
-                              // by the grouping kernel)
-    int part_rows;
-    const int* max_rows;      // heavy kernel: largest per-expert row count (written by the grouping kernel)
 };
 
 hipError_t launch_router_logits(const void* x, const void* w, int T, int H, int E, float* logits, hipStream_t st);
@@ -31,7 +25,7 @@ hipError_t launch_router_topk(const void* logits, bool bf16, int T, int E, int k
                               int32_t* ids, float* weights, hipStream_t st);
 size_t group_scratch_bytes(long long n, int El);
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
-                        int rows_estimate, int* sem,
+                        int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int cols, uint8_t* q, float* s,
@@ -41,7 +35,8 @@ hipError_t launch_grouped_gemm(bool gated, bool fp8, bool out_f32, const GemmArg
                                int max_tiles, int cus, hipStream_t st);
 hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows,
                                       int max_tiles, int cus, hipStream_t st);
-hipError_t launch_grouped_gemm_heavy(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,
+// heavy row tiles (up to 256 rows) with both operands tiled through LDS
+hipError_t launch_grouped_gemm_tiled(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,
                                      hipStream_t st);
 hipError_t launch_combine(const void* Y, const int32_t* inv_perm, const float* w, int T, int k, int H, void* out,
                           hipStream_t st);

@@ -32,7 +32,7 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
     tr = st["tile_rows"]
     assert tr in (16, 32) and (tr >= est or tr == 32)
     hr = st["heavy_rows"]
-    assert hr == 256  # bf16 weights (FP8 layers use 128)
+    assert hr == 256
     heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > tr))  # full heavy tiles and one with the rest
     light = int(sum(1 for c in ref["counts"] if 0 < c <= tr))
     assert st["heavy_tiles"] == heavy
