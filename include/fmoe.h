@@ -46,6 +46,7 @@ extern "C" {
 #define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
 #define FMOE_MAX_TOP_K 64         /* top_k                                                     */
 #define FMOE_MAX_DIM 65536        /* hidden and inter                                          */
+#define FMOE_MAX_ASSIGNMENTS (1 << 23) /* tokens * top_k                                       */
 
 typedef enum {
     FMOE_OK = 0,
@@ -59,7 +60,8 @@ typedef enum { FMOE_BF16 = 0, FMOE_FP32 = 1, FMOE_FP8_E4M3 = 2 } fmoe_dtype; /* 
 typedef enum { FMOE_SOFTMAX = 0, FMOE_SIGMOID = 1 } fmoe_scoring;
 
 /* Shape of one layer call.
- *   tokens  T >= 0        hidden H, inter I: positive multiples of 128, at most 65536
+ *   tokens  T >= 0, T*top_k <= FMOE_MAX_ASSIGNMENTS
+ *   hidden H, inter I: positive multiples of 128, at most 65536
  *   experts E (total physical expert slots, [H20] paragraph 3), 1 <= top_k <= min(E, 64)
  *   ep_size divides E; this rank owns experts [ep_rank*E/ep_size, (ep_rank+1)*E/ep_size)
  *   ([H20] paragraph 2); E_loc = E/ep_size <= 1024.

@@ -57,7 +57,7 @@ int check_shape(const fmoe_shape* s) {
     if (s->ep_size <= 0 || s->experts % s->ep_size || s->ep_rank < 0 || s->ep_rank >= s->ep_size) return FMOE_ERR_ARG;
     if (s->experts / s->ep_size > FMOE_MAX_EXPERTS || s->experts > FMOE_MAX_EXPERTS) return FMOE_ERR_UNSUPPORTED;
     if (s->weight_dtype != FMOE_BF16 && s->weight_dtype != FMOE_FP8_E4M3) return FMOE_ERR_UNSUPPORTED;
-    if ((long long)s->tokens * s->top_k > INT_MAX / 2) return FMOE_ERR_UNSUPPORTED;
+    if ((long long)s->tokens * s->top_k > FMOE_MAX_ASSIGNMENTS) return FMOE_ERR_UNSUPPORTED;
     return FMOE_OK;
 }
 

@@ -34,8 +34,10 @@ struct DevHeader {
 static_assert(sizeof(DevHeader) == 64, "header size");
 
 // One row tile of a grouped GEMM: local expert, first grouped row, number of rows.
+// Heavy tiles also carry, in `group`, their index among the heavy tiles of their expert (low
+// 16 bits) and that expert's heavy tile count (high 16 bits); light tiles carry 0.
 struct MTile {
-    int32_t expert, row0, rows, pad;
+    int32_t expert, row0, rows, group;
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -22,9 +22,10 @@
 // 4 + 4 double-width reads feed 16 MFMAs of 16x16x128 (FP8, one per 128-deep scale block,
 // whose product is added times weight scale x activation scale).
 //
-// Work order: tasks (row tile, column block) run column block fastest, and the persistent
-// workgroups of one XCD (workgroup ids equal mod 8) take consecutive tasks, so the tasks that
-// share a tile's activations or an expert's weights run at the same time behind one L2.
+// Work order: the tasks (row tile, column block) of one expert run column block first, then
+// tile, and the persistent workgroups of one XCD (workgroup ids equal mod 8) take consecutive
+// tasks, so the tiles that read the same weight block, and the column blocks that read the same
+// tile's activations, tend to run at the same time behind one L2.
 #include <type_traits>
 
 #include "launch.hpp"
@@ -97,10 +98,17 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
     for (int q = 0; q < 2; q++) frag[q] = tg_slot(r16, q * 4 + kg);
 
     for (int t = li; t < tasks; t += G) {
-        const int mt = t / nblocks;
-        const int nb = t - mt * nblocks;
-        // the tile list is read-only here: a scalar load through the constant address space
-        const i32x4 mv = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + mt);
+        // The tasks of an expert with m heavy tiles (tiles first .. first+m-1) are
+        // [first*nblocks, (first+m)*nblocks), ordered column block first, then tile: the m tiles
+        // that read the same weight block are consecutive tasks.  The tile list is read-only
+        // here: scalar loads through the constant address space.
+        const int i0 = t / nblocks;
+        const i32x4 m0 = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + i0);
+        const int m = m0[3] >> 16, first = i0 - (m0[3] & 0xffff);
+        const int tl = t - first * nblocks;
+        const int nb = tl / m;
+        const int tile = first + (tl - nb * m);
+        const i32x4 mv = tile == i0 ? m0 : *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + tile);
         const int expert = mv[0], row0 = mv[1], rows = mv[2];
         // every load of the previous task has landed and every wavefront is past its last
         // stage, so all buffers are free

@@ -202,7 +202,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
             mt.expert = e;
             mt.row0 = my_first;
             mt.rows = total;
-            mt.pad = 0;
+            mt.group = 0;
             mtiles[my_lfirst] = mt;
         }
         if (heavy) {
@@ -211,7 +211,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
                 mt.expert = e;
                 mt.row0 = my_first + j * hrows;
                 mt.rows = min(hrows, total - j * hrows);
-                mt.pad = 0;
+                mt.group = j | (nheavy << 16);  // nheavy <= 2^23 / 256
                 mtiles_heavy[my_hfirst + j] = mt;
             }
         }

@@ -47,6 +47,7 @@ def test_workspace_bytes_worst_case_and_growth():
     # the Y buffer alone is T*k*H*2 bytes; the workspace holds at least that
     assert ws_bytes(tokens=4096, hidden=2048, inter=768, experts=128, top_k=8) >= 4096 * 8 * 2048 * 2
     assert ws_bytes(tokens=32) > ws_bytes(tokens=16)
+    assert ws_bytes(tokens=1 << 22, top_k=2) > 0  # T*k = 2^23, the largest supported
     # fp8 keeps fp32 activations and codes on top of the bf16 layout
     assert ws_bytes(fp8=True) > 0
     # the size does not depend on the expert-parallel rank
@@ -66,6 +67,7 @@ def test_workspace_bytes_worst_case_and_growth():
     (dict(ep_size=2, ep_rank=2), fm.FMOE_ERR_ARG),
     (dict(experts=2048, top_k=2), fm.FMOE_ERR_UNSUPPORTED),
     (dict(experts=128, top_k=65), fm.FMOE_ERR_UNSUPPORTED),
+    (dict(tokens=(1 << 22) + 1, top_k=2), fm.FMOE_ERR_UNSUPPORTED),  # T*k above 2^23
 ])
 def test_workspace_bytes_rejects_bad_shapes(kw, code):
     base = dict(tokens=16, hidden=256, inter=128, experts=8, top_k=2)
