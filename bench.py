@@ -92,6 +92,42 @@ def build_inputs(wl: Workload, n_batches: int, n_copies: int):
     return shape, copies, batches, ws, out
 
 
+class HipEvent:
+    """A HIP timing event created without the system-scope fence (hipEventDisableSystemFence):
+    recording it does not write back and invalidate the caches, so an event between two kernels
+    costs about a microsecond instead of several and does not slow the kernel after it.  Passed
+    to the library by handle (`cuda_event`), like a torch.cuda.Event."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        h = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), HipEvent.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.cuda_event = h.value
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        import ctypes
+        f = ctypes.c_float()
+        if HipEvent._hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(self.cuda_event),
+                                             ctypes.c_void_p(end.cuda_event)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def __del__(self):
+        if self.cuda_event and HipEvent._hip is not None:
+            HipEvent._hip.hipEventDestroy(self.cuda_event)
+
+
 def pct(v, q):
     s = sorted(v)
     i = min(len(s) - 1, max(0, int(math.ceil(q / 100.0 * len(s))) - 1))
@@ -127,8 +163,8 @@ def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None):
     ev = []
     for _ in range(steps):
         e = [None] * (NS + 1)
-        e[pair[0]] = torch.cuda.Event(enable_timing=True)
-        e[pair[1]] = torch.cuda.Event(enable_timing=True)
+        e[pair[0]] = HipEvent()
+        e[pair[1]] = HipEvent()
         ev.append(e)
 
     def call(j, events=None):
@@ -145,8 +181,8 @@ def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None):
     wall = (time.perf_counter() - t0) / steps
     pair_us = [ev[i][pair[0]].elapsed_time(ev[i][pair[1]]) * 1e3 for i in range(steps)]
 
-    # stage breakdown: a separate pass with every event (each record adds a little time)
-    full = [[torch.cuda.Event(enable_timing=True) for _ in range(NS + 1)] for _ in range(steps)]
+    # stage breakdown: a separate pass with every event (each record adds about a microsecond)
+    full = [[HipEvent() for _ in range(NS + 1)] for _ in range(steps)]
     for i in range(steps):
         call(warmup + steps + i, full[i])
     torch.cuda.synchronize()

@@ -1,14 +1,14 @@
 // gemm_stream.hip -- grouped expert GEMMs for light row tiles (up to 32 rows), streaming form.
 //
 // Same operation as gemm.hip (gate/up with SiLU-and-mul, or down; bf16 or FP8 block-scaled),
-// for launches with enough tasks (row tile x 64 output features) to fill the GPU without
-// splitting the reduction.
+// for launches with enough tasks (row tile x 64 or 128 output features) to fill the GPU
+// without splitting the reduction.
 //
 // Decode is bound by the weight stream, so each wavefront is built as one uninterrupted
 // stream of weight loads: it walks its workgroup's tasks in order and its ring of D weight
 // steps (HBM straight into the MFMA "A" registers, 16 feature rows x 8 consecutive k per lane)
 // runs up to D steps ahead across task boundaries, so the stream never drains between tiles.
-// The tile's activation rows (the MFMA "B" operand) are the same for the 4 wavefronts of the
+// The tile's activation rows (the MFMA "B" operand) are the same for all wavefronts of the
 // workgroup: they are loaded once per workgroup, a chunk of CS reduction steps at a time,
 // through registers into a double-buffered LDS area (each 64-lane fragment is stored in the
 // lane order the MFMA reads it, so stores and reads are contiguous 16-byte accesses), with the
@@ -25,7 +25,7 @@ namespace fmoe {
 
 namespace {
 
-constexpr int kStreamFeatures = 64;  // output features per workgroup (4 wavefronts x 16)
+// A workgroup of WV wavefronts computes 16 WV output features of a row tile.
 
 template <bool FP8>
 struct SCfg {
@@ -78,15 +78,16 @@ struct Ctx {
     int soff;              // 0, or the step count for a padding context that re-reads the last step
 };
 
-template <bool GATED, bool FP8, bool OUT_F32, int NS, int D>
-__global__ __launch_bounds__(256) void k_grouped_gemm_stream(GemmArgs g) {
+template <bool GATED, bool FP8, bool OUT_F32, int NS, int D, int WV>
+__global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     using C = SCfg<FP8>;
     using FT = typename C::T;
     constexpr int NW = GATED ? 2 : 1;
     constexpr int CS = C::CS;
     constexpr int F = StreamLds<FP8, NS>::F;
-    constexpr int FPW = F / 4;  // pieces staged per wavefront
-    static_assert(F % 4 == 0 && CS % D == 0, "chunk shape");
+    constexpr int FPW = F / WV;  // pieces staged per wavefront
+    constexpr int FEAT = 16 * WV;
+    static_assert(F % WV == 0 && CS % D == 0, "chunk shape");
     __shared__ StreamLds<FP8, NS> L;
 
     const int lane = lane_id();
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_stream(GemmArgs g) {
     const int nsteps = K / C::KSTEP;
     const int nch = (nsteps + CS - 1) / CS;
     const int nkb = K >> 7;
-    const int nblocks = g.N / kStreamFeatures;
+    const int nblocks = g.N / FEAT;
     const int total = *g.tile_count * nblocks;
     if ((int)blockIdx.x >= total) return;
     const int ntasks = (total - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
@@ -128,11 +129,11 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_stream(GemmArgs g) {
         // (wavefront-uniform) read is a scalar load that does not wait on the weight stream
         const i32x4 mv = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + mt);
         const MTile m = {mv[0], mv[1], mv[2], mv[3]};
-        const size_t wrow = (size_t)m.expert * g.N + nb * kStreamFeatures + w * 16;
+        const size_t wrow = (size_t)m.expert * g.N + nb * FEAT + w * 16;
         c.w[0] = (const uint8_t*)g.W0 + wrow * rowbytes + lane_w;
         if constexpr (GATED) c.w[NW - 1] = (const uint8_t*)g.W1 + wrow * rowbytes + lane_w;
         if constexpr (FP8) {
-            const size_t srow = ((size_t)m.expert * (g.N >> 7) + ((nb * kStreamFeatures) >> 7)) * nkb;
+            const size_t srow = ((size_t)m.expert * (g.N >> 7) + ((nb * FEAT) >> 7)) * nkb;
             c.ws[0] = g.S0 + srow;
             if constexpr (GATED) c.ws[NW - 1] = g.S1 + srow;
         }
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_stream(GemmArgs g) {
     };
     auto task_n0 = [&](int i) {
         const int t = (int)blockIdx.x + i * (int)gridDim.x;
-        return (t % nblocks) * kStreamFeatures + w * 16;
+        return (t % nblocks) * FEAT + w * 16;
     };
 
     // Two context slots, used alternately (task i runs from slot i % 2 and reads ahead into
@@ -299,22 +300,28 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_stream(GemmArgs g) {
     }
 }
 
+// wavefronts per workgroup: 8 for the down GEMM (its short reduction makes the tile's staged
+// activation rows a large share of the traffic: 128 features share them instead of 64)
+template <bool GATED>
+constexpr int stream_waves() { return GATED ? 4 : 8; }
+
 template <bool GATED, bool FP8, bool OUT_F32, int NS>
 hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
     constexpr int D = FP8 ? 4 : 8;
+    constexpr int WV = stream_waves<GATED>();
     static int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D>, 256,
-                                                          0) != hipSuccess || nb < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV>,
+                                                          64 * WV, 0) != hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
     }
-    long long grid = (long long)max_tiles * (a.N / kStreamFeatures);
+    long long grid = (long long)max_tiles * (a.N / (16 * WV));
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D><<<(unsigned)grid, 256, 0, st>>>(a);
+    k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
     return hipGetLastError();
 }
 
