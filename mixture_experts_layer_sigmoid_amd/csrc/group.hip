@@ -26,7 +26,7 @@ namespace fmoe {
 constexpr int kScanThreads = 1024;
 constexpr int kSmallChunks = 64;  // chunks of the one-workgroup path
 constexpr int kSmallPerWave = kSmallChunks / (kScanThreads / 64);  // chunks per wavefront there
-constexpr int kScanShared = 32 + 1536;  // LDS ints of scan_and_tile
+constexpr int kScanShared = 96 + 64 + 1536;  // LDS ints of scan_and_tile (kScanLds + part sums)
 
 // Phase 1 for one chunk of 64 assignments, by one wavefront.  Writes the chunk's count of
 // every local expert to col[e * col_stride] (zeros included) and returns, for this lane, the
@@ -68,43 +68,58 @@ __device__ void chunk_rank(const int32_t* __restrict__ ids, int n, int E, int El
     *out_r = r;
 }
 
-// Exclusive sum over the kScanThreads threads of the workgroup (thread order); *total gets
-// the sum.  sh: 32 ints of LDS.
-__device__ int block_scan_excl(int v, int* sh, int* total) {
+// Exclusive sums of four values over the kScanThreads threads of the workgroup (thread
+// order), their totals, and the maximum of a fifth value, with three barriers.
+// sh: kScanLds ints of LDS.
+constexpr int kScanLds = 4 * 16 + 16 + 4 * 16 + 1;
+__device__ void block_scan4_max(const int (&v)[4], int mv, int* sh, int (&excl)[4], int (&total)[4], int* maxv) {
+    constexpr int NWV = kScanThreads / 64;
     const int lane = lane_id(), wid = threadIdx.x >> 6;
-    int x = v;
+    int x[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) x[i] = v[i];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int y = __shfl_up(x[i], o, 64);
+            if (lane >= o) x[i] += y;
+        }
     }
-    if (lane == 63) sh[wid] = x;
+    const int m = wave_max(mv);
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) sh[wid * 4 + i] = x[i];
+    }
+    if (lane == 0) sh[64 + wid] = m;
     __syncthreads();
     if (wid == 0) {
-        int t = lane < kScanThreads / 64 ? sh[lane] : 0;
+        int t[4];
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int y = __shfl_up(t, o, 64);
-            if (lane >= o) t += y;
+        for (int i = 0; i < 4; i++) t[i] = lane < NWV ? sh[lane * 4 + i] : 0;
+#pragma unroll
+        for (int o = 1; o < NWV; o <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int y = __shfl_up(t[i], o, 64);
+                if (lane >= o) t[i] += y;
+            }
         }
-        if (lane < kScanThreads / 64) sh[16 + lane] = t;
+        if (lane < NWV) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) sh[80 + lane * 4 + i] = t[i];
+        }
+        const int mm = wave_max(lane < NWV ? sh[64 + lane] : INT_MIN);
+        if (lane == 0) sh[80 + 4 * NWV] = mm;
     }
     __syncthreads();
-    const int res = x - v + (wid > 0 ? sh[16 + wid - 1] : 0);
-    *total = sh[16 + kScanThreads / 64 - 1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        excl[i] = x[i] - v[i] + (wid > 0 ? sh[80 + (wid - 1) * 4 + i] : 0);
+        total[i] = sh[80 + (NWV - 1) * 4 + i];
+    }
+    *maxv = sh[80 + 4 * NWV];
     __syncthreads();
-    return res;
-}
-
-__device__ int block_max(int v, int* sh) {
-    const int lane = lane_id(), wid = threadIdx.x >> 6;
-    v = wave_max(v);
-    if (lane == 0) sh[wid] = v;
-    __syncthreads();
-    int m = sh[0];
-    for (int q = 1; q < kScanThreads / 64; q++) m = max(m, sh[q]);
-    __syncthreads();
-    return m;
 }
 
 // Phase 2 by one workgroup of kScanThreads: turns cnt[c * El + e] (count of expert e in
@@ -136,7 +151,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
         }
         for (; c < c1; c++) s += cnt[c * El + e];
     }
-    int* part_sum = sh + 32;  // [kScanThreads], later 3 x [512]
+    int* part_sum = sh + kScanLds;  // [kScanThreads], later 3 x [512]
     part_sum[threadIdx.x] = s;
     __syncthreads();
     int before = 0, total = 0;  // this part's prefix inside its expert, and the expert total
@@ -154,11 +169,21 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
     const int hrows = heavy ? min(heavy_rows, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
     const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0
     int R, n_light, n_heavy, empty;
-    const int first = block_scan_excl(lead ? total : 0, sh, &R);  // valid in the lead thread
-    const int lfirst = block_scan_excl(lead && total > 0 && !heavy, sh, &n_light);
-    const int hfirst = block_scan_excl(lead ? nheavy : 0, sh, &n_heavy);
-    (void)block_scan_excl(lead && total == 0, sh, &empty);
-    const int max_rows = block_max(lead ? total : 0, sh);
+    // grouped rows, light tiles, heavy tiles and empty experts before each expert (valid in
+    // its lead thread), their totals, and the largest expert
+    int first, lfirst, hfirst, max_rows;
+    {
+        const int vals[4] = {lead ? total : 0, lead && total > 0 && !heavy, lead ? nheavy : 0, lead && total == 0};
+        int ex[4], tot[4];
+        block_scan4_max(vals, lead ? total : 0, sh, ex, tot, &max_rows);
+        first = ex[0];
+        lfirst = ex[1];
+        hfirst = ex[2];
+        R = tot[0];
+        n_light = tot[1];
+        n_heavy = tot[2];
+        empty = tot[3];
+    }
     // hand the lead thread's expert offset and first tiles to the other parts of the expert
     int* e_first = part_sum;           // [Ep]  (P > 1 means Ep <= 512; with P == 1 these are
     int* e_lfirst = part_sum + 512;    // [Ep]   never written)
