@@ -219,19 +219,29 @@ def fmoe_experts(shape: fmoe_shape, x: torch.Tensor, topk_ids: torch.Tensor, top
 
 def fmoe_forward(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights,
                  scoring: int = FMOE_SOFTMAX, renormalize: bool = True, ws: torch.Tensor | None = None,
-                 out: torch.Tensor | None = None, return_routing: bool = False, stage_events=None):
+                 out: torch.Tensor | None = None, return_routing: bool = False, stage_events=None,
+                 routing_out: tuple | None = None):
     """Whole layer -> out [T,H] bf16 (and (ids, weights) when return_routing).
 
-    stage_events: optional list of FMOE_NUM_STAGES+1 entries, each a
-    torch.cuda.Event(enable_timing=True) or None; when given, fmoe_forward_profiled records
-    the events around the stages (None entries are skipped)."""
+    routing_out: optional preallocated (ids [T,k] int32, weights [T,k] fp32) that receive the
+    routing (fixed buffers for graph capture); returned when return_routing.
+    stage_events: optional list of FMOE_NUM_STAGES+1 entries, each a timing event (an object
+    with a `cuda_event` handle, such as torch.cuda.Event(enable_timing=True)) or None; when
+    given, fmoe_forward_profiled records the events around the stages (None entries are
+    skipped)."""
     _dev(x, "x", torch.bfloat16)
     _dev(logits, "logits")
     dev = x.device
     ws = workspace(shape, dev) if ws is None else ws
     out = torch.empty((shape.tokens, shape.hidden), dtype=torch.bfloat16, device=dev) if out is None else out
     ids = wts = None
-    if return_routing:
+    if routing_out is not None:
+        ids, wts = routing_out
+        _dev(ids, "routing ids", torch.int32)
+        _dev(wts, "routing weights", torch.float32)
+        if ids.shape != (shape.tokens, shape.top_k) or wts.shape != (shape.tokens, shape.top_k):
+            raise ValueError("routing_out must be ([T, k] int32, [T, k] float32)")
+    elif return_routing:
         ids = torch.empty((shape.tokens, shape.top_k), dtype=torch.int32, device=dev)
         wts = torch.empty((shape.tokens, shape.top_k), dtype=torch.float32, device=dev)
     ws_struct = w.struct()
