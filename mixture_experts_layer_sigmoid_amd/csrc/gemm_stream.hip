@@ -46,12 +46,12 @@ struct SCfg<true> {
     static constexpr int CS = 4;
 };
 
-template <bool FP8, int NS>
+template <bool FP8, int NS, int CS>
 struct StreamLds {
-    static constexpr int F = NS * SCfg<FP8>::CS * SCfg<FP8>::HALVES;  // 1 KB pieces per chunk
+    static constexpr int F = NS * CS * SCfg<FP8>::HALVES;  // 1 KB pieces per chunk
     i32x4 x[2][F][64];
-    float asc[2][SCfg<FP8>::CS][NS * 16];  // FP8: activation scale of each step and tile row
-    float wsc[2][2][SCfg<FP8>::CS];        // FP8: weight-block scale of each matrix and step
+    float asc[2][CS][NS * 16];  // FP8: activation scale of each step and tile row
+    float wsc[2][2][CS];        // FP8: weight-block scale of each matrix and step
 };
 
 __device__ __forceinline__ float silu_mul_s(float g, float u) { return g / (1.0f + expf(-g)) * u; }
@@ -78,17 +78,16 @@ struct Ctx {
     int soff;              // 0, or the step count for a padding context that re-reads the last step
 };
 
-template <bool GATED, bool FP8, bool OUT_F32, int NS, int D, int WV>
+template <bool GATED, bool FP8, bool OUT_F32, int NS, int D, int WV, int CS>
 __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     using C = SCfg<FP8>;
     using FT = typename C::T;
     constexpr int NW = GATED ? 2 : 1;
-    constexpr int CS = C::CS;
-    constexpr int F = StreamLds<FP8, NS>::F;
+    constexpr int F = StreamLds<FP8, NS, CS>::F;
     constexpr int FPW = F / WV;  // pieces staged per wavefront
     constexpr int FEAT = 16 * WV;
     static_assert(F % WV == 0 && CS % D == 0, "chunk shape");
-    __shared__ StreamLds<FP8, NS> L;
+    __shared__ StreamLds<FP8, NS, CS> L;
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -305,14 +304,13 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
 template <bool GATED>
 constexpr int stream_waves() { return GATED ? 4 : 8; }
 
-template <bool GATED, bool FP8, bool OUT_F32, int NS>
+template <bool GATED, bool FP8, bool OUT_F32, int NS, int CS, int D>
 hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
-    constexpr int D = FP8 ? 4 : 8;
     constexpr int WV = stream_waves<GATED>();
     static int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV, CS>,
                                                           64 * WV, 0) != hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
@@ -321,14 +319,25 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
+    k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV, CS><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
     return hipGetLastError();
 }
 
+// Chunk length CS and weight ring depth D: bf16 8 and 8, FP8 4 and 4.  An FP8 down GEMM on
+// 32-row tiles whose reduction is a multiple of 6 steps (768 deep: 6 steps) takes chunks of 6
+// with a ring of 3 instead, so no chunk is padded past the reduction end (a third of the
+// steps with chunks of 4); measured 10% faster there.
 template <bool GATED, bool FP8, bool OUT_F32>
 hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, int cus, hipStream_t st) {
-    if (tile_rows == 16) return launch_stream<GATED, FP8, OUT_F32, 1>(a, max_tiles, cus, st);
-    if (tile_rows == 32) return launch_stream<GATED, FP8, OUT_F32, 2>(a, max_tiles, cus, st);
+    constexpr int CS = SCfg<FP8>::CS, D = FP8 ? 4 : 8;
+    if (tile_rows == 16) return launch_stream<GATED, FP8, OUT_F32, 1, CS, D>(a, max_tiles, cus, st);
+    if (tile_rows == 32) {
+        if constexpr (FP8 && !GATED) {
+            const int nsteps = a.K / SCfg<FP8>::KSTEP;
+            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT_F32, 2, 6, 3>(a, max_tiles, cus, st);
+        }
+        return launch_stream<GATED, FP8, OUT_F32, 2, CS, D>(a, max_tiles, cus, st);
+    }
     return hipErrorInvalidValue;
 }
 
