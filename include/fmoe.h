@@ -153,6 +153,32 @@ int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int
                  int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes,
                  void* stream);
 
+/* Tile plan for tuning harnesses (the tile-space sweep of bench.py).  The host heuristic picks
+ * the largest light row tile from the rows-per-expert estimate max(1, ceil(T*top_k/E)) ("vLLM
+ * Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel Selection",
+ * paragraphs 3-4) and the reduction split from the expected task count; a nonzero field here
+ * replaces that choice:
+ *   tile_rows      largest rows of a light row tile: 16 or 32 (experts with more rows are cut
+ *                  into heavy tiles on the device)
+ *   split_gate_up  wavefronts that split the reduction of a light tile in the gate/up GEMM:
+ *                  1 (the streaming kernel), 2 or 4
+ *   split_down     the same for the down GEMM */
+typedef struct {
+    int32_t tile_rows, split_gate_up, split_down;
+} fmoe_plan;
+
+/* fmoe_forward with the nonzero fields of *plan (NULL: none) in place of the heuristic's
+ * choices.  FMOE_ERR_ARG for a field outside the values above; FMOE_ERR_UNSUPPORTED when an
+ * FP8 layer's 32-row tile would not fit the activation scales of a split tile in 64 KB of LDS
+ * (the limit the heuristic also applies).  fmoe_workspace_bytes(shape) fits every plan.
+ * Results equal fmoe_forward's within the layer's rounding (the reduction order of a split
+ * tile differs). */
+int fmoe_forward_planned(const fmoe_shape* shape, const void* x, const void* logits,
+                         int32_t logits_dtype, int32_t scoring, int32_t renormalize,
+                         const fmoe_weights* w, void* out, int32_t* topk_ids_out,
+                         float* topk_weights_out, void* ws, size_t ws_bytes, void* stream,
+                         const fmoe_plan* plan);
+
 /* Stages of fmoe_forward, in launch order, for fmoe_forward_profiled. */
 enum {
     FMOE_STAGE_ROUTER = 0, FMOE_STAGE_GROUP = 1, FMOE_STAGE_QUANT_X = 2,

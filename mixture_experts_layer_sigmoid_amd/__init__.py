@@ -23,7 +23,7 @@ FMOE_NUM_STAGES = 9
 STAGES = ("router", "group", "quant_x", "gemm1", "gemm1_heavy", "quant_h", "gemm2", "gemm2_heavy", "combine")
 EXPORTED = ("fmoe_abi_version", "fmoe_status_string", "fmoe_workspace_bytes", "fmoe_router_logits",
             "fmoe_router_topk", "fmoe_route_permute", "fmoe_experts", "fmoe_forward", "fmoe_forward_profiled",
-            "fmoe_read_stats")
+            "fmoe_forward_planned", "fmoe_read_stats")
 
 
 class fmoe_shape(ctypes.Structure):
@@ -35,6 +35,12 @@ class fmoe_shape(ctypes.Structure):
 class fmoe_weights(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p)]
+
+
+class fmoe_plan(ctypes.Structure):
+    """Tile plan overrides (0 keeps the heuristic's choice): tile_rows 16/32, split_gate_up and
+    split_down 1 (streaming kernel), 2 or 4 wavefronts per reduction."""
+    _fields_ = [("tile_rows", ctypes.c_int32), ("split_gate_up", ctypes.c_int32), ("split_down", ctypes.c_int32)]
 
 
 class fmoe_stats(ctypes.Structure):
@@ -68,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmoe_forward.argtypes = [ctypes.POINTER(fmoe_shape), P, P, i32, i32, i32, ctypes.POINTER(fmoe_weights), P,
                                  P, P, P, sz, P]
     lib.fmoe_forward_profiled.argtypes = lib.fmoe_forward.argtypes + [P]
+    lib.fmoe_forward_planned.argtypes = lib.fmoe_forward.argtypes + [ctypes.POINTER(fmoe_plan)]
     lib.fmoe_read_stats.argtypes = [P, P, ctypes.POINTER(fmoe_stats)]
     for name in EXPORTED:
         if name != "fmoe_status_string":
@@ -220,7 +227,7 @@ def fmoe_experts(shape: fmoe_shape, x: torch.Tensor, topk_ids: torch.Tensor, top
 def fmoe_forward(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights,
                  scoring: int = FMOE_SOFTMAX, renormalize: bool = True, ws: torch.Tensor | None = None,
                  out: torch.Tensor | None = None, return_routing: bool = False, stage_events=None,
-                 routing_out: tuple | None = None):
+                 routing_out: tuple | None = None, plan: fmoe_plan | None = None):
     """Whole layer -> out [T,H] bf16 (and (ids, weights) when return_routing).
 
     routing_out: optional preallocated (ids [T,k] int32, weights [T,k] fp32) that receive the
@@ -228,7 +235,9 @@ def fmoe_forward(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: Ex
     stage_events: optional list of FMOE_NUM_STAGES+1 entries, each a timing event (an object
     with a `cuda_event` handle, such as torch.cuda.Event(enable_timing=True)) or None; when
     given, fmoe_forward_profiled records the events around the stages (None entries are
-    skipped)."""
+    skipped).
+    plan: optional fmoe_plan; when given, fmoe_forward_planned replaces the heuristic's tile
+    choices with its nonzero fields (not combined with stage_events)."""
     _dev(x, "x", torch.bfloat16)
     _dev(logits, "logits")
     dev = x.device
@@ -248,7 +257,11 @@ def fmoe_forward(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: Ex
     args = [ctypes.byref(shape), _ptr(x), _ptr(logits), _dtype_code(logits), scoring, int(bool(renormalize)),
             ctypes.byref(ws_struct), _ptr(out), _ptr(ids), _ptr(wts), _ptr(ws), ws.numel(), _stream(dev)]
     lib = load_library()
-    if stage_events is None:
+    if plan is not None:
+        if stage_events is not None:
+            raise ValueError("plan and stage_events cannot be combined")
+        _check("fmoe_forward_planned", lib.fmoe_forward_planned(*args, ctypes.byref(plan)))
+    elif stage_events is None:
         _check("fmoe_forward", lib.fmoe_forward(*args))
     else:
         if len(stage_events) != FMOE_NUM_STAGES + 1:

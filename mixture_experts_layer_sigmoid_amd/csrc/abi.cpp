@@ -61,7 +61,8 @@ int check_shape(const fmoe_shape* s) {
     return FMOE_OK;
 }
 
-Plan make_plan(const fmoe_shape* s) {
+// ov: tile plan overrides (nullptr: the heuristic alone); checked by check_plan first.
+Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr) {
     Plan p;
     p.T = s->tokens;
     p.H = s->hidden;
@@ -82,6 +83,7 @@ Plan make_plan(const fmoe_shape* s) {
     while (tr < need && tr < kLightRows) tr <<= 1;
     // FP8 stages the tile's activation scales in LDS: keep them within 64 KB
     while (p.fp8 && tr > 16 && gemm_lds_bytes(true, p.H > p.I ? p.H : p.I, tr) > 65536) tr >>= 1;
+    if (ov && ov->tile_rows) tr = ov->tile_rows;
     p.tile_rows = tr;
     // Split the reduction over 2 or 4 wavefronts when the expected tiles (about one per
     // active expert under uniform routing) times the 16-feature blocks leave the GPU's
@@ -92,13 +94,15 @@ Plan make_plan(const fmoe_shape* s) {
         const long long tasks = active * (N / 16);
         return tasks < 1024 ? 4 : (tasks < 2048 ? 2 : 1);
     };
-    p.wk1 = pick_wk(p.I);
-    p.wk2 = pick_wk(p.H);
-    // light tiles: one per expert with 1..tile_rows rows; heavy tiles: ceil(c/128) per expert
-    // with c > tile_rows rows, at most n/128 + (n / (tile_rows + 1)) in all; no tile is empty
+    p.wk1 = ov && ov->split_gate_up ? ov->split_gate_up : pick_wk(p.I);
+    p.wk2 = ov && ov->split_down ? ov->split_down : pick_wk(p.H);
+    // light tiles: one per expert with 1..tile_rows rows; heavy tiles: ceil(c/heavy_rows) per
+    // expert with c > tile_rows rows, at most n/heavy_rows + n/(tile_rows+1) in all (bounded
+    // with the smallest light tile, 16 rows, so one workspace fits every tile plan); no tile
+    // is empty
     const long long nl = p.El < p.n ? p.El : p.n;
     p.heavy_rows = heavy_max_rows(p.fp8);
-    long long nh = p.n / p.heavy_rows + (p.n / (tr + 1) < p.El ? p.n / (tr + 1) : p.El) + 1;
+    long long nh = p.n / p.heavy_rows + (p.n / 17 < p.El ? p.n / 17 : p.El) + 1;
     if (nh > p.n) nh = p.n;
     p.max_light = (int)(nl < 1 ? 1 : nl);
     p.max_heavy = (int)(nh < 1 ? 1 : nh);
@@ -249,14 +253,27 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     return FMOE_OK;
 }
 
+// Values a tile plan may force; the FP8 split kernel's LDS limit for 32-row tiles.
+int check_plan(const fmoe_shape* s, const fmoe_plan* ov) {
+    if (!ov) return FMOE_OK;
+    auto split_ok = [](int v) { return v == 0 || v == 1 || v == 2 || v == 4; };
+    if (!(ov->tile_rows == 0 || ov->tile_rows == 16 || ov->tile_rows == 32)) return FMOE_ERR_ARG;
+    if (!split_ok(ov->split_gate_up) || !split_ok(ov->split_down)) return FMOE_ERR_ARG;
+    const int K = s->hidden > s->inter ? s->hidden : s->inter;
+    if (s->weight_dtype == FMOE_FP8_E4M3 && ov->tile_rows == 32 && gemm_lds_bytes(true, K, 32) > 65536)
+        return FMOE_ERR_UNSUPPORTED;
+    return FMOE_OK;
+}
+
 int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t logits_dtype, int32_t scoring,
                  int32_t renormalize, const fmoe_weights* w, void* out, int32_t* ids_out, float* wts_out, void* ws,
-                 size_t ws_bytes, void* stream, void* const* ev) {
+                 size_t ws_bytes, void* stream, void* const* ev, const fmoe_plan* ov = nullptr) {
     int rc = check_shape(s);
     if (rc) return rc;
+    if ((rc = check_plan(s, ov))) return rc;
     if (logits_dtype != FMOE_BF16 && logits_dtype != FMOE_FP32) return FMOE_ERR_UNSUPPORTED;
     if (scoring != FMOE_SOFTMAX && scoring != FMOE_SIGMOID) return FMOE_ERR_ARG;
-    Plan p = make_plan(s);
+    Plan p = make_plan(s, ov);
     if ((rc = check_weights(p, w))) return rc;
     if (p.T == 0) return FMOE_OK;
     if (!x || !logits || !out || !ws) return FMOE_ERR_ARG;
@@ -361,6 +378,14 @@ int fmoe_forward_profiled(const fmoe_shape* shape, const void* x, const void* lo
     if (!stage_events) return FMOE_ERR_ARG;
     return forward_impl(shape, x, logits, logits_dtype, scoring, renormalize, w, out, topk_ids_out,
                         topk_weights_out, ws, ws_bytes, stream, stage_events);
+}
+
+int fmoe_forward_planned(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype,
+                         int32_t scoring, int32_t renormalize, const fmoe_weights* w, void* out,
+                         int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes, void* stream,
+                         const fmoe_plan* plan) {
+    return forward_impl(shape, x, logits, logits_dtype, scoring, renormalize, w, out, topk_ids_out,
+                        topk_weights_out, ws, ws_bytes, stream, nullptr, plan);
 }
 
 int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {

@@ -126,3 +126,26 @@ def test_zero_tokens_is_a_no_op():
     assert lib.fmoe_router_topk(None, 0, 0, 8, 2, 0, 1, None, None, None) == fm.FMOE_OK
     assert lib.fmoe_router_logits(None, None, 0, 256, 8, None, None) == fm.FMOE_OK
     assert lib.fmoe_route_permute(ctypes.byref(s), None, None, None, None, None, None, 0, None) == fm.FMOE_OK
+
+
+def test_forward_planned_rejects_bad_plans_before_launching():
+    lib = fm.load_library()
+    P = ctypes.c_void_p
+    s = fm.make_shape(16, 256, 128, 8, 2)
+    w = fm.fmoe_weights(0x1000, 0x2000, 0x3000, None, None, None)
+    ws_n = fm.fmoe_workspace_bytes(s)
+
+    def call(shape, weights, plan):
+        return lib.fmoe_forward_planned(ctypes.byref(shape), P(0x100), P(0x100), 0, 0, 1, ctypes.byref(weights),
+                                        P(0x300), None, None, P(0x400), fm.fmoe_workspace_bytes(shape), None,
+                                        ctypes.byref(plan))
+    for bad in (fm.fmoe_plan(24, 0, 0), fm.fmoe_plan(0, 3, 0), fm.fmoe_plan(0, 0, 8), fm.fmoe_plan(-16, 1, 1)):
+        assert call(s, w, bad) == fm.FMOE_ERR_ARG
+    # FP8 with a 65536-deep reduction: 32-row tiles would need 68 KB of activation scales in LDS
+    s8 = fm.make_shape(16, 65536, 128, 8, 2, fp8=True)
+    w8 = fm.fmoe_weights(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
+    assert call(s8, w8, fm.fmoe_plan(32, 0, 0)) == fm.FMOE_ERR_UNSUPPORTED
+    # a plan with zero tokens is still a no-op
+    s0 = fm.make_shape(0, 256, 128, 8, 2)
+    assert lib.fmoe_forward_planned(ctypes.byref(s0), None, None, 0, 0, 1, ctypes.byref(w), None, None, None, None, 0,
+                                    None, ctypes.byref(fm.fmoe_plan(16, 4, 2))) == fm.FMOE_OK

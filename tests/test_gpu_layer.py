@@ -7,7 +7,7 @@ import torch
 import mixture_experts_layer_sigmoid_amd as fm
 import oracle
 from mixture_experts_layer_sigmoid_amd import synth
-from gpu_common import BF16_TOL, FP8_TOL, Layer, announce, check_layer, row_rel_err
+from gpu_common import BF16_TOL, FP8_TOL, Layer, announce, check_layer, row_rel_err, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,23 @@ def test_profiled_forward_and_hip_graph_replays_match_eager():
         assert torch.equal(out, eager), f"replay {i}"
         # eager work between the replays
         assert torch.equal(fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws), eager)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_every_tile_plan_matches_the_oracle(fp8):
+    announce(f"all 18 tile plans (tile rows x gate/up split x down split), concentrated, fp8={fp8}")
+    T, H, I, E, k = 130, 384, 256, 32, 8
+    L = Layer(config=101, T=T, H=H, I=I, E=E, k=k, fp8=fp8, routing="concentrated")
+    ids_ref, w_ref = L.oracle_routing()
+    ref = L.oracle_tokens(ids_ref, w_ref, sample_tokens(T, 10 ** 6))
+    ws = fm.workspace(L.shape)
+    for tr in (16, 32):
+        for s1 in (1, 2, 4):
+            for s2 in (1, 2, 4):
+                out, ids, _ = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, return_routing=True,
+                                              plan=fm.fmoe_plan(tr, s1, s2))
+                assert np.array_equal(ids.cpu().numpy(), ids_ref)
+                st = fm.fmoe_read_stats(ws)
+                assert st["tile_rows"] == tr and st["heavy_tiles"] > 0
+                err = row_rel_err(out.float().cpu().numpy(), ref)
+                assert err <= (FP8_TOL if fp8 else BF16_TOL), f"plan ({tr}, {s1}, {s2}): {err:.3e}"
