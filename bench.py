@@ -114,6 +114,16 @@ class HipEvent:
             raise RuntimeError("hipEventCreateWithFlags failed")
         self.cuda_event = h.value
 
+    def record(self):
+        """Record on torch's current stream."""
+        import ctypes
+
+        import torch
+        HipEvent._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        if HipEvent._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_time(self, end: "HipEvent") -> float:
         """Milliseconds from this event to `end` (both recorded and complete)."""
         import ctypes
@@ -273,6 +283,61 @@ def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
                        f"OpenMP over tokens, {threads} threads on {platform.processor() or platform.machine()}")
 
 
+def tile_sweep(workloads, steps: int = 10) -> list:
+    """Tile-space sweep: every tile plan the library can run (light tile rows 16/32 x gate/up
+    reduction split 1/2/4 x down split 1/2/4) against the host heuristic, per workload.  Each
+    variant: 2 warmup calls, then `steps` back-to-back calls timed between two events (GPU
+    time per call), weights rotating over the workload's copies."""
+    import torch
+
+    import mixture_experts_layer_sigmoid_amd as fm
+
+    # the heuristic runs first and last (the faster of the two counts), after a warmup of its own
+    plans = [None] + [(tr, s1, s2) for tr in (16, 32) for s1 in (1, 2, 4) for s2 in (1, 2, 4)] + [None]
+    out = []
+    for wl in workloads:
+        print(f"[bench] tile sweep: {wl.name}", file=sys.stderr, flush=True)
+        touched_guess = wl.El * (1 - (1 - wl.k / wl.E) ** wl.T) * wl.expert_bytes()
+        n_copies = max(2, min(8, int(math.ceil(2 * CACHE_BYTES / max(touched_guess, 1))) + 1))
+        shape, copies, batches, ws, o = build_inputs(wl, max(4, n_copies), n_copies)
+        times = {}
+        for j in range(20):  # warmup: clocks, caches, the library's first-launch queries
+            x, lg = batches[j % len(batches)]
+            fm.fmoe_forward(shape, x, lg, copies[j % n_copies], ws=ws, out=o)
+        for plan in plans:
+            fp = None if plan is None else fm.fmoe_plan(*plan)
+
+            def call(j):
+                x, lg = batches[j % len(batches)]
+                try:
+                    fm.fmoe_forward(shape, x, lg, copies[j % n_copies], ws=ws, out=o, plan=fp)
+                    return True
+                except RuntimeError:  # a plan this shape cannot take (FP8 LDS limit)
+                    return False
+            if not (call(0) and call(1)):
+                continue
+            a, b = HipEvent(), HipEvent()
+            torch.cuda.synchronize()
+            a.record()
+            for j in range(steps):
+                call(2 + j)
+            b.record()
+            torch.cuda.synchronize()
+            key = "heuristic" if plan is None else "tile %d, split %d/%d" % plan
+            t = a.elapsed_time(b) * 1e3 / steps
+            times[key] = min(t, times.get(key, t))
+        best = min((v, k) for k, v in times.items() if k != "heuristic")
+        rec = dict(workload=wl.name, heuristic_us=round(times["heuristic"], 1), best_plan=best[1],
+                   best_us=round(best[0], 1), heuristic_over_best=round(times["heuristic"] / best[0], 3),
+                   worst_us=round(max(times.values()), 1), plans_us={k: round(v, 1) for k, v in times.items()})
+        print(f"[bench]   heuristic {rec['heuristic_us']} us, best {rec['best_plan']} {rec['best_us']} us "
+              f"(x{rec['heuristic_over_best']})", file=sys.stderr, flush=True)
+        out.append(rec)
+        del copies, batches, ws, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def sweep_workloads(B3, synth):
     """The T sweep of the bf16 layer (uniform and concentrated), the FP8 w8a8 layer, and the FP8
     expert-parallel shard; the headline workload is not repeated."""
@@ -315,6 +380,9 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 256 MiB device copy (torch elementwise kernel): the reference launch "
                          "for scaling hardware byte counters")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every tile plan against the heuristic on the sweep workloads (tuning report; "
+                         "prints one JSON line, no headline)")
     ap.add_argument("--workload", default=None,
                     help="run only the sweep workloads whose name contains this text (profiling); no headline")
     args = ap.parse_args()
@@ -338,6 +406,13 @@ def main():
         del src, dst
     B3 = synth.BF16_LAYER
     head = Workload("bf16 H2048 I768 E128 top8, T=256, uniform", config=B3, T=256, H=2048, I=768, E=128, k=8)
+    if args.tile_sweep:
+        wls = [head] + sweep_workloads(B3, synth)
+        if args.workload is not None:
+            wls = [wl for wl in wls if args.workload in wl.name]
+        print(json.dumps(dict(metric="tile-space sweep: µs/call per tile plan vs the heuristic",
+                              results=tile_sweep(wls))))
+        return
     if args.workload is not None:
         picked = [wl for wl in [head] + sweep_workloads(B3, synth) if args.workload in wl.name]
         rows = []

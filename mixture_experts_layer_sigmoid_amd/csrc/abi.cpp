@@ -77,25 +77,34 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr) {
     p.rows_estimate = (int)(est < 1 ? 1 : est);
     // Largest row tile: the estimate plus three standard deviations of the per-expert count
     // under uniform routing (about sqrt(estimate)), so a uniform batch rarely cuts an expert
-    // in two; heavier experts get more tiles on the device.
+    // in two; heavier experts get more tiles on the device.  From 32 expected rows per expert
+    // on, most experts exceed a light tile anyway, and the tile-space sweep (bench.py
+    // --tile-sweep) measured the smallest light tile best there (every expert above 16 rows
+    // goes to the heavy-tile kernel): 270 against 304 us at T=512 of the 128-expert layer.
     const double need = p.rows_estimate + 3.0 * std::sqrt((double)p.rows_estimate) + 1.0;
     int tr = 16;
     while (tr < need && tr < kLightRows) tr <<= 1;
+    if (p.rows_estimate >= 32) tr = 16;
     // FP8 stages the tile's activation scales in LDS: keep them within 64 KB
     while (p.fp8 && tr > 16 && gemm_lds_bytes(true, p.H > p.I ? p.H : p.I, tr) > 65536) tr >>= 1;
     if (ov && ov->tile_rows) tr = ov->tile_rows;
     p.tile_rows = tr;
-    // Split the reduction over 2 or 4 wavefronts when the expected tiles (about one per
-    // active expert under uniform routing) times the 16-feature blocks leave the GPU's
-    // 1024 SIMDs with fewer than two wavefronts each.
+    // Split the reduction over 4 wavefronts when the expected tiles (about one per active
+    // expert under uniform routing) times the 16-feature blocks leave the GPU's 1024 SIMDs
+    // with fewer than one wavefront each.  Otherwise the streaming kernel (no split), except
+    // where the tile-space sweep measured a split of 2 faster (bf16 weights): the gate/up GEMM
+    // below 16 expected rows per expert (T=8: 133 -> 118 us, T=32: 225 -> 212 us), the down
+    // GEMM at one expected row (T=8: 118 -> 111 us); FP8 tiles stream best unsplit there.
     const long long local_rows = (p.n * p.El + p.E - 1) / p.E;
     const long long active = local_rows < p.El ? local_rows : p.El;
-    auto pick_wk = [&](int N) {
+    auto pick_wk = [&](int N, bool gate_up) {
         const long long tasks = active * (N / 16);
-        return tasks < 1024 ? 4 : (tasks < 2048 ? 2 : 1);
+        if (tasks < 1024) return 4;
+        if (!p.fp8 && (gate_up ? p.rows_estimate < 16 : p.rows_estimate <= 1)) return 2;
+        return tasks < 2048 ? 2 : 1;
     };
-    p.wk1 = ov && ov->split_gate_up ? ov->split_gate_up : pick_wk(p.I);
-    p.wk2 = ov && ov->split_down ? ov->split_down : pick_wk(p.H);
+    p.wk1 = ov && ov->split_gate_up ? ov->split_gate_up : pick_wk(p.I, true);
+    p.wk2 = ov && ov->split_down ? ov->split_down : pick_wk(p.H, false);
     // light tiles: one per expert with 1..tile_rows rows; heavy tiles: ceil(c/heavy_rows) per
     // expert with c > tile_rows rows, at most n/heavy_rows + n/(tile_rows+1) in all (bounded
     // with the smallest light tile, 16 rows, so one workspace fits every tile plan); no tile

@@ -61,10 +61,12 @@ class Layer:
         self.logits_gpu = self.logits.cuda()
         self.shape = fm.make_shape(T, H, I, E, k, ep_size, ep_rank, fp8)
 
+    plan = None  # an fmoe_plan to force tile choices (None: the library's heuristic)
+
     def forward(self, ws=None):
         sc = fm.FMOE_SOFTMAX if self.scoring == "softmax" else fm.FMOE_SIGMOID
         return fm.fmoe_forward(self.shape, self.x_gpu, self.logits_gpu, self.w, sc, self.renorm, ws=ws,
-                               return_routing=True)
+                               return_routing=True, plan=self.plan)
 
     def oracle_routing(self):
         return oracle.router_topk(synth.bf16_bits(self.logits), self.k, self.scoring, self.renorm)

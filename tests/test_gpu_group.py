@@ -30,10 +30,12 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
     est = max(1, -(-T * k // E))
     assert st["rows_estimate"] == est
     tr = st["tile_rows"]
-    assert tr in (16, 32) and (tr >= est or tr == 32)
+    # light tile: covers the estimate up to 32 rows; from 32 expected rows on, the smallest
+    # (every expert above 16 rows goes to the heavy-tile kernel)
+    assert tr in (16, 32) and (tr == 16 if est >= 32 else (tr >= est or tr == 32))
     hr = st["heavy_rows"]
     assert hr == 256
-    heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > tr))  # full heavy tiles and one with the rest
+    heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > tr))  # ceil(c / 256) equal tiles per heavy expert
     light = int(sum(1 for c in ref["counts"] if 0 < c <= tr))
     assert st["heavy_tiles"] == heavy
     assert st["m_tiles"] == light + heavy

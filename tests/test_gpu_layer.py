@@ -50,9 +50,9 @@ def test_fp8_layer_small(T, H, I, E, k, ep):
     check_layer(L, n_sample=10 ** 6)
 
 
-# Shapes whose plans run the streaming light kernel (no split reduction) for GEMM1 and/or GEMM2,
-# covering 16- and 32-row tiles, single-chunk reductions, chunks padded past the reduction end
-# (bf16 chunks of 8 steps, FP8 of 4) and an expert-parallel shard.
+# The streaming light kernel (no split reduction, forced by the tile plan) on shapes covering
+# 16- and 32-row tiles, single-chunk reductions, chunks padded past the reduction end (bf16
+# chunks of 8 steps, FP8 of 4 or 6) and an expert-parallel shard.
 @pytest.mark.parametrize("T,H,I,E,k,ep,fp8", [
     (64, 256, 512, 64, 8, 1, False),    # GEMM1 streamed, one chunk, 32-row tiles
     (40, 1024, 384, 64, 4, 1, False),   # GEMM2 streamed, 12 steps in 2 chunks, 16-row tiles
@@ -63,6 +63,7 @@ def test_fp8_layer_small(T, H, I, E, k, ep):
 def test_layer_streaming_kernel_shapes(T, H, I, E, k, ep, fp8):
     announce(f"streaming-kernel shape T={T} H={H} I={I} E={E} k={k} ep={ep} fp8={fp8}")
     L = Layer(config=94, T=T, H=H, I=I, E=E, k=k, fp8=fp8, ep_size=ep, ep_rank=ep - 1)
+    L.plan = fm.fmoe_plan(0, 1, 1)
     check_layer(L, n_sample=10 ** 6)
 
 
