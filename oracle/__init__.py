@@ -48,6 +48,7 @@ def _load():
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         lib.oracle_router_logits.argtypes = [P, P, i, i, i, P]
         lib.oracle_router_topk.argtypes = [P, i, i, i, i, i, i, P, P]
+        lib.oracle_router_topk_grouped.argtypes = [P, i, i, i, i, i, i, i, i, P, P]
         lib.oracle_rows_per_expert_estimate.restype = i
         lib.oracle_rows_per_expert_estimate.argtypes = [ctypes.c_longlong] * 3
         lib.oracle_route_permute.argtypes = [i, i, i, i, i, P, P, P, P, P, P]
@@ -104,6 +105,24 @@ def router_topk(logits: np.ndarray, k: int, scoring: str = "softmax", renorm: bo
     w = np.empty((T, k), np.float64)
     _load().oracle_router_topk(_p(lg), int(is_bf16), T, E, k, 0 if scoring == "softmax" else 1,
                                int(bool(renorm)), _p(ids), _p(w))
+    return ids, w
+
+
+def router_topk_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int, scoring: str = "softmax",
+                        renorm: bool = True, is_bf16: bool | None = None):
+    """Grouped (group-limited) top-k, the definition in oracle.c: keep the topk_group groups
+    (of E/n_group consecutive experts) with the largest best logit, then plain top-k among
+    their experts.  logits [T,E] fp32 or uint16 bf16 bits -> (ids int32 [T,k], weights float64)."""
+    if is_bf16 is None:
+        is_bf16 = logits.dtype == np.uint16
+    lg = _c(logits, np.uint16 if is_bf16 else np.float32)
+    T, E = lg.shape
+    if n_group < 1 or E % n_group or not 1 <= topk_group <= n_group or k > topk_group * (E // n_group):
+        raise ValueError("need E % n_group == 0, 1 <= topk_group <= n_group, k <= topk_group * E / n_group")
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    _load().oracle_router_topk_grouped(_p(lg), int(is_bf16), T, E, k, n_group, topk_group,
+                                       0 if scoring == "softmax" else 1, int(bool(renorm)), _p(ids), _p(w))
     return ids, w
 
 

@@ -156,6 +156,86 @@ void oracle_router_topk(const void* logits, int is_bf16, int T, int E, int k, in
     free(taken);
 }
 
+/* Grouped (group-limited) top-k.  [PR39593] names a grouped top-k beside the plain one without
+ * defining it; this is the plain reading, written out (and listed with the other readings of
+ * the pages):
+ *   1. the E experts form n_group groups of E/n_group consecutive indices;
+ *   2. a group's key is the largest sanitised logit among its experts;
+ *   3. the topk_group groups with the largest keys are kept, the lower group index first
+ *      among equal keys;
+ *   4. the k ids are picked as in oracle_router_topk, among the kept groups' experts only;
+ *   5. the weights are those of oracle_router_topk for these ids (softmax without
+ *      renormalisation still normalises over all E experts).
+ * Requires E % n_group == 0, 1 <= topk_group <= n_group and k <= topk_group * E / n_group,
+ * so the k ids are distinct.  With n_group == 1 or topk_group == n_group it is
+ * oracle_router_topk. */
+void oracle_router_topk_grouped(const void* logits, int is_bf16, int T, int E, int k, int n_group, int topk_group,
+                                int scoring, int renorm, int32_t* ids, double* w) {
+    const int gsz = E / n_group;
+    float* v = (float*)malloc(sizeof(float) * (size_t)E);
+    char* taken = (char*)malloc((size_t)E);
+    float* gkey = (float*)malloc(sizeof(float) * (size_t)n_group);
+    char* gkept = (char*)malloc((size_t)n_group);
+    for (int t = 0; t < T; t++) {
+        for (int e = 0; e < E; e++) {
+            float raw = is_bf16 ? oracle_bf16_to_f32(((const uint16_t*)logits)[(size_t)t * E + e])
+                                : ((const float*)logits)[(size_t)t * E + e];
+            v[e] = sanitize(raw);
+        }
+        /* step 2: group keys */
+        for (int g = 0; g < n_group; g++) {
+            gkey[g] = v[g * gsz];
+            for (int e = g * gsz + 1; e < (g + 1) * gsz; e++)
+                if (v[e] > gkey[g]) gkey[g] = v[e];
+            gkept[g] = 0;
+        }
+        /* step 3: topk_group rounds of "largest remaining key, lowest group among equals" */
+        for (int j = 0; j < topk_group; j++) {
+            int best = -1;
+            for (int g = 0; g < n_group; g++) {
+                if (gkept[g]) continue;
+                if (best < 0 || gkey[g] > gkey[best]) best = g;
+            }
+            gkept[best] = 1;
+        }
+        /* step 4: the plain selection, with the experts of dropped groups already taken */
+        for (int e = 0; e < E; e++) taken[e] = !gkept[e / gsz];
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                if (best < 0 || v[e] > v[best]) best = e;
+            }
+            taken[best] = 1;
+            ids[(size_t)t * k + j] = best;
+        }
+        /* step 5: weights as the plain router */
+        const int32_t* id = ids + (size_t)t * k;
+        double* wt = w + (size_t)t * k;
+        if (scoring == 0) {
+            double m = v[0];
+            for (int e = 1; e < E; e++) if (v[e] > m) m = v[e];
+            double denom = 0.0;
+            if (renorm) for (int j = 0; j < k; j++) denom += exp((double)v[id[j]] - m);
+            else for (int e = 0; e < E; e++) denom += exp((double)v[e] - m);
+            for (int j = 0; j < k; j++) wt[j] = exp((double)v[id[j]] - m) / denom;
+        } else {
+            double sum = 0.0;
+            for (int j = 0; j < k; j++) {
+                wt[j] = 1.0 / (1.0 + exp(-(double)v[id[j]]));
+                sum += wt[j];
+            }
+            if (renorm) {
+                for (int j = 0; j < k; j++) wt[j] = (sum > 0.0) ? wt[j] / sum : 1.0 / k;
+            }
+        }
+    }
+    free(v);
+    free(taken);
+    free(gkey);
+    free(gkept);
+}
+
 /* ------------------------------------------------------------------ grouping */
 
 /* Rows per expert estimate of [H20] paragraph 3: ceil(tokens * top_k / total physical

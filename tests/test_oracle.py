@@ -397,3 +397,56 @@ def test_duplicate_ids_become_two_rows():
     out = oracle.moe_tokens(xb, ids, w, *wb, E=E)
     one = oracle.moe_tokens(xb, np.array([[2], [1], [0]], np.int32), np.ones((3, 1)), *wb, E=E)
     assert np.allclose(out[0], one[0], rtol=1e-14) and np.allclose(out[2], 2 * one[2], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- grouped (group-limited) top-k
+
+def test_grouped_router_worked_example():
+    import json
+    with open(os.path.join(GOLDEN, "router_grouped_example.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        lg = np.array([[float(v) for v in c["logits"]]], np.float32)
+        ids, w = oracle.router_topk_grouped(lg, c["k"], g["n_group"], c["topk_group"])
+        assert ids[0].tolist() == c["ids"], c["note"]
+        v = np.nan_to_num(lg[0].astype(np.float64), nan=-np.finfo(np.float32).max)[ids[0]]
+        e = np.exp(v - v.max())
+        np.testing.assert_allclose(w[0], e / e.sum(), rtol=1e-12, atol=0)  # renormalised softmax closed form
+
+
+@pytest.mark.parametrize("E,n_group,k,scoring,renorm", [(64, 1, 6, "softmax", True), (256, 8, 8, "sigmoid", True),
+                                                         (128, 4, 5, "softmax", False), (32, 32, 4, "sigmoid", False)])
+def test_grouped_router_with_every_group_kept_is_the_plain_router(E, n_group, k, scoring, renorm):
+    lg = synth.bf16_bits(synth.router_batch(96, E, k, seed=7))
+    ids, w = oracle.router_topk_grouped(lg, k, n_group, n_group, scoring, renorm)
+    ids_p, w_p = oracle.router_topk(lg, k, scoring, renorm)
+    assert np.array_equal(ids, ids_p)
+    np.testing.assert_allclose(w, w_p, rtol=1e-12, atol=1e-300)
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,k", [(256, 8, 4, 8), (64, 16, 3, 6), (128, 4, 1, 8), (30, 5, 2, 7)])
+def test_grouped_router_matches_stable_argsort_formulation(E, n_group, topk_group, k):
+    rng = np.random.default_rng(E * 100 + n_group)
+    lg = rng.standard_normal((200, E)).astype(np.float32)
+    lg[rng.random(lg.shape) < 0.05] = np.nan
+    lg[3] = np.nan  # an all-NaN row
+    lg[5] = 0.5     # an all-equal row
+    lg[7, :] = np.round(lg[7, :])  # many ties
+    ids, _ = oracle.router_topk_grouped(lg, k, n_group, topk_group)
+    v = np.where(np.isnan(lg), -np.finfo(np.float32).max, lg)
+    gsz = E // n_group
+    for t in range(lg.shape[0]):
+        gkey = v[t].reshape(n_group, gsz).max(axis=1)
+        kept = np.argsort(-gkey, kind="stable")[:topk_group]  # larger key first, lower group among equals
+        allowed = np.concatenate([np.arange(g * gsz, (g + 1) * gsz) for g in sorted(kept)])
+        order = allowed[np.argsort(-v[t, allowed], kind="stable")]
+        assert ids[t].tolist() == order[:k].tolist(), t
+        assert len(set(ids[t].tolist())) == k
+    assert ids[3].tolist() == list(range(k))
+
+
+def test_grouped_router_rejects_impossible_shapes():
+    lg = np.zeros((2, 12), np.float32)
+    for k, ng, tg in ((3, 5, 2), (3, 4, 0), (3, 4, 5), (7, 4, 2)):
+        with pytest.raises(ValueError):
+            oracle.router_topk_grouped(lg, k, ng, tg)
