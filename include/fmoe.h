@@ -122,6 +122,21 @@ int fmoe_router_topk(const void* logits, int32_t logits_dtype, int32_t T, int32_
                      int32_t scoring, int32_t renormalize, int32_t* topk_ids, float* topk_weights,
                      void* stream);
 
+/* Grouped (group-limited) top-k router.  The experts form n_group groups of E/n_group
+ * consecutive indices; a group's key is its largest sanitised logit; the topk_group groups with
+ * the largest keys are kept (the lower group first among equal keys); the k ids are then picked
+ * as in fmoe_router_topk among the kept groups' experts only, with the same weights (an
+ * unrenormalised softmax still divides by all E).  "PR #39593: [Bug]: Fix FlashInfer CUTLASS
+ * BF16 + CUDA graphs IMA", Root cause, names this router beside the plain one; the definition
+ * is the reading taken here.  Requires E % n_group == 0, 1 <= n_group <= 64,
+ * 1 <= topk_group <= n_group and k <= topk_group * E / n_group (FMOE_ERR_ARG otherwise;
+ * n_group > 64: FMOE_ERR_UNSUPPORTED), so the k ids are distinct; all-NaN rows give 0..k-1.
+ * topk_group == n_group is fmoe_router_topk.  Buffers, dtypes and errors otherwise as
+ * fmoe_router_topk. */
+int fmoe_router_topk_grouped(const void* logits, int32_t logits_dtype, int32_t T, int32_t E, int32_t k,
+                             int32_t n_group, int32_t topk_group, int32_t scoring, int32_t renormalize,
+                             int32_t* topk_ids, float* topk_weights, void* stream);
+
 /* Per-expert grouping of the T*k assignments topk_ids [T,k] for this rank (shape gives
  * T, E, k, ep_size, ep_rank; H, I and weight_dtype are used only to size the workspace):
  *   counts [E_loc]      rows per local expert

@@ -23,7 +23,7 @@ FMOE_NUM_STAGES = 9
 STAGES = ("router", "group", "quant_x", "gemm1", "gemm1_heavy", "quant_h", "gemm2", "gemm2_heavy", "combine")
 EXPORTED = ("fmoe_abi_version", "fmoe_status_string", "fmoe_workspace_bytes", "fmoe_router_logits",
             "fmoe_router_topk", "fmoe_route_permute", "fmoe_experts", "fmoe_forward", "fmoe_forward_profiled",
-            "fmoe_forward_planned", "fmoe_read_stats")
+            "fmoe_forward_planned", "fmoe_router_topk_grouped", "fmoe_read_stats")
 
 
 class fmoe_shape(ctypes.Structure):
@@ -69,6 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmoe_workspace_bytes.argtypes = [ctypes.POINTER(fmoe_shape), ctypes.POINTER(sz)]
     lib.fmoe_router_logits.argtypes = [P, P, i32, i32, i32, P, P]
     lib.fmoe_router_topk.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.fmoe_router_topk_grouped.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P]
     lib.fmoe_route_permute.argtypes = [ctypes.POINTER(fmoe_shape), P, P, P, P, P, P, sz, P]
     lib.fmoe_experts.argtypes = [ctypes.POINTER(fmoe_shape), P, P, P, ctypes.POINTER(fmoe_weights), P, P, sz, P]
     lib.fmoe_forward.argtypes = [ctypes.POINTER(fmoe_shape), P, P, i32, i32, i32, ctypes.POINTER(fmoe_weights), P,
@@ -187,6 +188,20 @@ def fmoe_router_topk(logits: torch.Tensor, k: int, scoring: int = FMOE_SOFTMAX, 
     _check("fmoe_router_topk",
            load_library().fmoe_router_topk(_ptr(logits), _dtype_code(logits), T, E, k, scoring, int(bool(renormalize)),
                                            _ptr(ids), _ptr(wts), _stream(logits.device)))
+    return ids, wts
+
+
+def fmoe_router_topk_grouped(logits: torch.Tensor, k: int, n_group: int, topk_group: int,
+                             scoring: int = FMOE_SOFTMAX, renormalize: bool = True):
+    """Grouped (group-limited) top-k: logits [T,E] bf16 or fp32 -> (ids int32 [T,k], weights fp32 [T,k])."""
+    _dev(logits, "logits")
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("fmoe_router_topk_grouped",
+           load_library().fmoe_router_topk_grouped(_ptr(logits), _dtype_code(logits), T, E, k, n_group, topk_group,
+                                                   scoring, int(bool(renormalize)), _ptr(ids), _ptr(wts),
+                                                   _stream(logits.device)))
     return ids, wts
 
 

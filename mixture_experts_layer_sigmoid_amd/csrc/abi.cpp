@@ -343,6 +343,22 @@ int fmoe_router_topk(const void* logits, int32_t logits_dtype, int32_t T, int32_
                                          topk_ids, topk_weights, (hipStream_t)stream));
 }
 
+int fmoe_router_topk_grouped(const void* logits, int32_t logits_dtype, int32_t T, int32_t E, int32_t k,
+                             int32_t n_group, int32_t topk_group, int32_t scoring, int32_t renormalize,
+                             int32_t* topk_ids, float* topk_weights, void* stream) {
+    if (T < 0 || E <= 0 || k <= 0 || k > E) return FMOE_ERR_ARG;
+    if (E > FMOE_MAX_EXPERTS || k > FMOE_MAX_TOP_K) return FMOE_ERR_UNSUPPORTED;
+    if (n_group > 64) return FMOE_ERR_UNSUPPORTED;
+    if (n_group < 1 || E % n_group || topk_group < 1 || topk_group > n_group) return FMOE_ERR_ARG;
+    if ((long long)k > (long long)topk_group * (E / n_group)) return FMOE_ERR_ARG;
+    if (logits_dtype != FMOE_BF16 && logits_dtype != FMOE_FP32) return FMOE_ERR_UNSUPPORTED;
+    if (scoring != FMOE_SOFTMAX && scoring != FMOE_SIGMOID) return FMOE_ERR_ARG;
+    if (T == 0) return FMOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return FMOE_ERR_ARG;
+    return hip_status(launch_router_topk(logits, logits_dtype == FMOE_BF16, T, E, k, scoring, renormalize != 0,
+                                         topk_ids, topk_weights, (hipStream_t)stream, n_group, topk_group));
+}
+
 int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
                        int32_t* perm_src, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_shape(shape);

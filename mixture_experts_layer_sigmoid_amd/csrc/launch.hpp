@@ -21,8 +21,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_router_logits(const void* x, const void* w, int T, int H, int E, float* logits, hipStream_t st);
+// n_group groups of E/n_group experts, topk_group of them kept (n_group = topk_group = 1: plain top-k)
 hipError_t launch_router_topk(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
-                              int32_t* ids, float* weights, hipStream_t st);
+                              int32_t* ids, float* weights, hipStream_t st, int n_group = 1, int topk_group = 1);
 size_t group_scratch_bytes(long long n, int El);
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
                         int rows_estimate,

@@ -7,6 +7,13 @@
 // 64-lane wavefront owns one token row: the row sits in registers (expert e in lane e%64,
 // slot e/64), each of the k rounds is a 64-bit max-reduction across the wavefront, and
 // the picked lane retires its slot, so ids are distinct by construction.
+//
+// Grouped (group-limited) top-k: the pages name it beside the plain router without defining
+// it; the reading taken: experts form n_group groups of consecutive indices, a group's key is
+// its best expert key (largest sanitised logit, and among equal values the lower expert, so
+// the lower group), the topk_group best groups are kept, and the plain k rounds then run over
+// the kept groups' experts only.  One max-reduction per group, one per kept group, and the
+// dropped groups' slots are retired before the k rounds.
 #include <float.h>
 
 #include "launch.hpp"
@@ -46,8 +53,8 @@ __device__ __forceinline__ float key_float(uint32_t kb) {
 
 template <int SLOTS, bool BF16_IN>
 __global__ __launch_bounds__(256) void k_router_topk(const void* __restrict__ logits, int T, int E, int k,
-                                                     int scoring, int renorm, int32_t* __restrict__ ids,
-                                                     float* __restrict__ weights) {
+                                                     int scoring, int renorm, int n_group, int topk_group,
+                                                     int32_t* __restrict__ ids, float* __restrict__ weights) {
     const int lane = lane_id();
     const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wavefront leaves together
@@ -67,6 +74,31 @@ __global__ __launch_bounds__(256) void k_router_topk(const void* __restrict__ lo
         key[s] = (e < E) ? (((unsigned long long)float_key(v[s]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
     }
 
+    if (topk_group < n_group) {  // grouped: retire the slots of the groups not kept
+        const int gsz = E / n_group;
+        int grp[SLOTS];
+#pragma unroll
+        for (int s = 0; s < SLOTS; s++) grp[s] = (lane + 64 * s < E) ? (lane + 64 * s) / gsz : 0;  // past E: key 0
+        unsigned long long gk = 0ull;  // lane g < n_group holds the key of group g
+        for (int g = 0; g < n_group; g++) {
+            unsigned long long b = 0ull;
+#pragma unroll
+            for (int s = 0; s < SLOTS; s++) b = (grp[s] == g && key[s] > b) ? key[s] : b;
+            b = wave_max(b);
+            if (lane == g) gk = b;
+        }
+        unsigned long long kept = 0ull;  // bit g: group g kept
+        for (int j = 0; j < topk_group; j++) {
+            const unsigned long long b = wave_max(gk);  // group keys are distinct (distinct experts)
+            const int g = __ffsll((long long)__ballot(gk == b && b != 0ull)) - 1;
+            kept |= 1ull << g;
+            if (lane == g) gk = 0ull;
+        }
+#pragma unroll
+        for (int s = 0; s < SLOTS; s++)
+            if (!((kept >> grp[s]) & 1ull)) key[s] = 0ull;
+    }
+
     float my_v = -FLT_MAX;  // lane j < k keeps the value of pick j
     int my_id = 0;
     for (int j = 0; j < k; j++) {
@@ -82,7 +114,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const void* __restrict__ lo
             if (lane + 64 * s == e) key[s] = 0ull;
     }
 
-    const float m = __shfl(my_v, 0, 64);  // the first pick holds the row maximum
+    const float m = __shfl(my_v, 0, 64);  // the first pick holds the row maximum (its group is kept)
     float w = 0.0f;
     if (scoring == 0) {
         float ex = (lane < k) ? expf(my_v - m) : 0.0f;
@@ -120,23 +152,24 @@ hipError_t launch_router_logits(const void* x, const void* w, int T, int H, int 
 }
 
 template <int SLOTS>
-static void launch_topk_slots(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
-                              int32_t* ids, float* weights, hipStream_t st) {
+static void launch_topk_slots(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm, int ng,
+                              int tg, int32_t* ids, float* weights, hipStream_t st) {
     int blocks = (T + 3) / 4;
     if (bf16)
-        k_router_topk<SLOTS, true><<<blocks, 256, 0, st>>>(logits, T, E, k, scoring, renorm, ids, weights);
+        k_router_topk<SLOTS, true><<<blocks, 256, 0, st>>>(logits, T, E, k, scoring, renorm, ng, tg, ids, weights);
     else
-        k_router_topk<SLOTS, false><<<blocks, 256, 0, st>>>(logits, T, E, k, scoring, renorm, ids, weights);
+        k_router_topk<SLOTS, false><<<blocks, 256, 0, st>>>(logits, T, E, k, scoring, renorm, ng, tg, ids, weights);
 }
 
 hipError_t launch_router_topk(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
-                              int32_t* ids, float* weights, hipStream_t st) {
+                              int32_t* ids, float* weights, hipStream_t st, int n_group, int topk_group) {
     int slots = (E + 63) / 64;
-    if (slots <= 1) launch_topk_slots<1>(logits, bf16, T, E, k, scoring, renorm, ids, weights, st);
-    else if (slots <= 2) launch_topk_slots<2>(logits, bf16, T, E, k, scoring, renorm, ids, weights, st);
-    else if (slots <= 4) launch_topk_slots<4>(logits, bf16, T, E, k, scoring, renorm, ids, weights, st);
-    else if (slots <= 8) launch_topk_slots<8>(logits, bf16, T, E, k, scoring, renorm, ids, weights, st);
-    else launch_topk_slots<16>(logits, bf16, T, E, k, scoring, renorm, ids, weights, st);
+    const int ng = n_group, tg = topk_group;
+    if (slots <= 1) launch_topk_slots<1>(logits, bf16, T, E, k, scoring, renorm, ng, tg, ids, weights, st);
+    else if (slots <= 2) launch_topk_slots<2>(logits, bf16, T, E, k, scoring, renorm, ng, tg, ids, weights, st);
+    else if (slots <= 4) launch_topk_slots<4>(logits, bf16, T, E, k, scoring, renorm, ng, tg, ids, weights, st);
+    else if (slots <= 8) launch_topk_slots<8>(logits, bf16, T, E, k, scoring, renorm, ng, tg, ids, weights, st);
+    else launch_topk_slots<16>(logits, bf16, T, E, k, scoring, renorm, ng, tg, ids, weights, st);
     return hipGetLastError();
 }
 

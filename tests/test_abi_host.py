@@ -149,3 +149,16 @@ def test_forward_planned_rejects_bad_plans_before_launching():
     s0 = fm.make_shape(0, 256, 128, 8, 2)
     assert lib.fmoe_forward_planned(ctypes.byref(s0), None, None, 0, 0, 1, ctypes.byref(w), None, None, None, None, 0,
                                     None, ctypes.byref(fm.fmoe_plan(16, 4, 2))) == fm.FMOE_OK
+
+
+def test_grouped_router_rejects_bad_groups_before_launching():
+    lib = fm.load_library()
+    P = ctypes.c_void_p
+    call = lambda E, k, ng, tg: lib.fmoe_router_topk_grouped(P(0x100), 0, 4, E, k, ng, tg, 0, 1, P(0x200),
+                                                             P(0x300), None)
+    assert call(64, 4, 5, 2) == fm.FMOE_ERR_ARG        # 5 does not divide 64
+    assert call(64, 4, 8, 0) == fm.FMOE_ERR_ARG        # no group kept
+    assert call(64, 4, 8, 9) == fm.FMOE_ERR_ARG        # more groups kept than exist
+    assert call(64, 9, 8, 1) == fm.FMOE_ERR_ARG        # 8 experts in one kept group < k
+    assert call(256, 4, 128, 2) == fm.FMOE_ERR_UNSUPPORTED  # more than 64 groups
+    assert lib.fmoe_router_topk_grouped(P(0x100), 0, 0, 64, 4, 8, 2, 0, 1, None, None, None) == fm.FMOE_OK  # T = 0

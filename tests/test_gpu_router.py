@@ -87,3 +87,34 @@ def test_router_is_deterministic():
     for _ in range(20):
         again = fm.fmoe_router_topk(lg, 8, fm.FMOE_SIGMOID, True)
         assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1])
+
+
+@pytest.mark.parametrize("E,ng,tg,k,scoring,renorm,fp32", [
+    (128, 8, 3, 8, "softmax", True, False),    # the NaN / tie batch, 16 experts per group
+    (256, 8, 4, 8, "sigmoid", True, False),    # 256 experts in 8 groups, 4 kept
+    (64, 16, 3, 6, "softmax", False, True),
+    (400, 8, 4, 6, "sigmoid", False, True),    # 50 experts per group, groups across slots
+    (1024, 64, 2, 8, "softmax", True, False),  # 64 groups (the most), 16 slots per lane
+    (30, 5, 2, 7, "softmax", True, True),      # E not a multiple of 64
+])
+def test_grouped_router_matches_oracle(E, ng, tg, k, scoring, renorm, fp32):
+    announce(f"grouped router E={E} groups={ng} kept={tg} k={k} {scoring} renorm={renorm} fp32={fp32}")
+    lg = synth.router_batch(128, E, k, seed=11)
+    if fp32:
+        lg = lg.float()
+    ids, w = fm.fmoe_router_topk_grouped(lg.cuda(), k, ng, tg, SCORING[scoring], renorm)
+    torch.cuda.synchronize()
+    ref_in = lg.numpy() if fp32 else synth.bf16_bits(lg)
+    ids_ref, w_ref = oracle.router_topk_grouped(ref_in, k, ng, tg, scoring, renorm)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.abs(w.cpu().numpy() - w_ref).max() <= WEIGHT_TOL
+
+
+def test_grouped_router_with_every_group_kept_is_the_plain_kernel():
+    announce("grouped router, every group kept, vs plain router kernel")
+    lg = synth.router_batch(128, 128, 8, seed=12).cuda()
+    for ng in (1, 4, 32):
+        a = fm.fmoe_router_topk_grouped(lg, 8, ng, ng)
+        b = fm.fmoe_router_topk(lg, 8)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
