@@ -184,9 +184,10 @@ void record(void* const* ev, int i, hipStream_t st) {
 
 // Grouping, expert GEMMs and combine for routing already in ids/wts (device pointers).
 // max_expert_rows bounds the rows of one expert: T when the router made the ids (distinct
-// experts per token), T*k for ids from the caller.
+// experts per token), T*k for ids from the caller.  grouped: the fused router + grouping
+// launch has already written the grouping.
 int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* wts, const fmoe_weights* w, void* out,
-                char* ws, hipStream_t st, void* const* ev, long long max_expert_rows) {
+                char* ws, hipStream_t st, void* const* ev, long long max_expert_rows, bool grouped = false) {
     const Layout& L = p.L;
     DevHeader* hdr = (DevHeader*)(ws + L.hdr);
     int32_t* perm = (int32_t*)(ws + L.perm);
@@ -196,7 +197,8 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
 
     record(ev, FMOE_STAGE_GROUP, st);
     MTile* mtiles_heavy = mtiles + p.max_light;
-    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.heavy_rows, p.rows_estimate,
+    if (!grouped)
+        FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.heavy_rows, p.rows_estimate,
                           (int32_t*)(ws + L.counts),
                           (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
                           mtiles_heavy, hdr, st));
@@ -293,8 +295,17 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
     int32_t* ids = ids_out ? ids_out : (int32_t*)(wsb + p.L.ids);
     float* wts = wts_out ? wts_out : (float*)(wsb + p.L.wts);
     record(ev, FMOE_STAGE_ROUTER, st);
-    FMOE_TRY(launch_router_topk(logits, logits_dtype == FMOE_BF16, p.T, p.E, p.k, scoring, renormalize != 0, ids,
-                                wts, st));
+    const bool bf16 = logits_dtype == FMOE_BF16;
+    if (route_group_fits((int)p.T, p.k, p.E, p.El)) {  // small batch: router and grouping in one launch
+        const Layout& L = p.L;
+        MTile* mtiles = (MTile*)(wsb + L.mtiles);
+        FMOE_TRY(launch_route_group(logits, bf16, (int)p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, p.El, p.lo,
+                                    p.tile_rows, p.heavy_rows, p.rows_estimate, (int32_t*)(wsb + L.counts),
+                                    (int32_t*)(wsb + L.offsets), (int32_t*)(wsb + L.perm), (int32_t*)(wsb + L.inv),
+                                    mtiles, mtiles + p.max_light, (DevHeader*)(wsb + L.hdr), st));
+        return run_experts(p, x, ids, wts, w, out, wsb, st, ev, p.T, true);
+    }
+    FMOE_TRY(launch_router_topk(logits, bf16, p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, st));
     return run_experts(p, x, ids, wts, w, out, wsb, st, ev, p.T);
 }
 

@@ -97,9 +97,37 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     const int nch = (nsteps + CS - 1) / CS;
     const int nkb = K >> 7;
     const int nblocks = g.N / FEAT;
-    const int total = *g.tile_count * nblocks;
-    if ((int)blockIdx.x >= total) return;
-    const int ntasks = (total - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+    const int mtc = *g.tile_count;
+    // Task order.  Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the 8
+    // XCDs in turn), and every XCD has its own L2.  With at least 8 row tiles, tile m goes to
+    // XCD m % 8 and all its feature blocks run there, so the tile's activation rows are fetched
+    // into one L2 instead of up to eight; the workgroups of an XCD deal its tasks in turn.
+    // With fewer tiles, tasks are dealt over all workgroups in order (spread over the XCDs).
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const bool by_xcd = (G % 8 == 0) && mtc >= 8;
+    const int xcd = b % 8, slot = b / 8, S = G / 8;
+    int ntasks;
+    if (by_xcd) {
+        const int ntx = ((mtc - xcd + 7) / 8) * nblocks;  // tasks of this XCD
+        ntasks = ntx > slot ? (ntx - 1 - slot) / S + 1 : 0;
+    } else {
+        const int total = mtc * nblocks;
+        ntasks = total > b ? (total - 1 - b) / G + 1 : 0;
+    }
+    if (ntasks == 0) return;
+    // tile and feature block of this workgroup's task i
+    auto task_at = [&](int i, int& mt, int& nb) {
+        if (by_xcd) {
+            const int j = slot + i * S;
+            const int q = j / nblocks;
+            mt = xcd + 8 * q;
+            nb = j - q * nblocks;
+        } else {
+            const int t = b + i * G;
+            mt = t / nblocks;
+            nb = t - mt * nblocks;
+        }
+    };
     const size_t rowbytes = (size_t)K * C::EB;
     const size_t lane_w = (size_t)r16 * rowbytes + kg * C::LANE_B;
 
@@ -121,9 +149,8 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             c.soff = nsteps;
             return;
         }
-        const int t = (int)blockIdx.x + i * (int)gridDim.x;
-        const int mt = t / nblocks;
-        const int nb = t - mt * nblocks;
+        int mt, nb;
+        task_at(i, mt, nb);
         // the tile list is read-only here: read it through the constant address space, so the
         // (wavefront-uniform) read is a scalar load that does not wait on the weight stream
         const i32x4 mv = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + mt);
@@ -247,8 +274,9 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
         }
     };
     auto task_n0 = [&](int i) {
-        const int t = (int)blockIdx.x + i * (int)gridDim.x;
-        return (t % nblocks) * FEAT + w * 16;
+        int mt, nb;
+        task_at(i, mt, nb);
+        return nb * FEAT + w * 16;
     };
 
     // Two context slots, used alternately (task i runs from slot i % 2 and reads ahead into
@@ -318,7 +346,7 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
     long long grid = (long long)max_tiles * (a.N / (16 * WV));
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
-    if (grid < 1) grid = 1;
+    grid = (grid + 7) / 8 * 8;  // a multiple of 8 for the per-XCD task order (extra workgroups exit)
     k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV, CS><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
     return hipGetLastError();
 }

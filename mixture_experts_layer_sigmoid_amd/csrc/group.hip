@@ -20,6 +20,7 @@
 // batch) is cut into tiles of at most 256 rows for the heavy kernel, rows spread as evenly as
 // 16-row steps allow.
 #include "launch.hpp"
+#include "router_row.hpp"
 
 namespace fmoe {
 
@@ -270,14 +271,13 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 
 // ---------------------------------------------------------------- one-workgroup path
 
-__global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
-                                                             int lo, int tile_rows, int heavy_rows, int rows_estimate,
-                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ perm_src,
-                                                             int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
-                                                             MTile* __restrict__ mtiles_heavy,
-                                                             DevHeader* __restrict__ hdr) {
-    extern __shared__ int lds[];
+// All three phases by one workgroup of kScanThreads.  ids may point to global memory or to
+// LDS (generic addressing); lds holds small_lds_ints(n, El) ints.
+__device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, int El, int lo, int tile_rows,
+                                            int heavy_rows, int rows_estimate, int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+                                            int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
+                                            MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr, int* lds) {
     const int nchunk = (n + 63) / 64;  // <= kSmallChunks
     constexpr int NW = kScanThreads / 64;
     int* cnt = lds;                        // [nchunk][El]
@@ -308,6 +308,45 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
         if (c < nchunk)
             chunk_scatter(c * 64 + lane_id(), n, l[j], r[j], l[j] >= 0 ? cnt[c * El + l[j]] : 0, perm_src, inv_perm);
     }
+}
+
+static size_t small_lds_ints(int n, int El) {
+    const int nchunk = (n + 63) / 64;
+    return (size_t)El * nchunk + (size_t)(kScanThreads / 64) * El + kSmallChunks + kScanShared;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
+                                                             int lo, int tile_rows, int heavy_rows, int rows_estimate,
+                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm_src,
+                                                             int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
+                                                             MTile* __restrict__ mtiles_heavy,
+                                                             DevHeader* __restrict__ hdr) {
+    extern __shared__ int lds[];
+    group_small(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm, mtiles,
+                mtiles_heavy, hdr, lds);
+}
+
+// Router top-k and grouping in one launch for at most kFusedTokens tokens: wavefront t routes
+// token t (plain top-k, the router kernel's row code), writing ids and weights to global memory
+// and the ids to LDS as well; after one barrier the workgroup groups the ids from LDS.
+constexpr int kFusedTokens = kScanThreads / 64;
+
+template <int SLOTS, bool BF16_IN>
+__global__ __launch_bounds__(kScanThreads) void k_route_group_small(
+    const void* __restrict__ logits, int T, int E, int k, int scoring, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int El, int lo, int tile_rows, int heavy_rows, int rows_estimate,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
+    DevHeader* __restrict__ hdr) {
+    extern __shared__ int lds[];
+    const int n = T * k;
+    int* ids_lds = lds;  // [n], padded to 4 ints
+    const int w = threadIdx.x >> 6;
+    if (w < T) topk_row<SLOTS, BF16_IN>(logits, w, E, k, scoring, renorm, 1, 1, ids, weights, ids_lds + w * k);
+    __syncthreads();
+    group_small(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm,
+                mtiles, mtiles_heavy, hdr, lds + ((n + 3) & ~3));
 }
 
 // ---------------------------------------------------------------- multi-workgroup path
@@ -368,7 +407,7 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
-    const size_t lds = (size_t)(El * nchunk + (kScanThreads / 64) * El + kSmallChunks + kScanShared) * 4;
+    const size_t lds = small_lds_ints(n, El) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
         k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts,
                                                     offsets,
@@ -382,6 +421,45 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
                                              offsets, mtiles,
                                              mtiles_heavy, hdr);
     k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);
+    return hipGetLastError();
+}
+
+static size_t route_group_lds_bytes(int T, int k, int El) {
+    const int n = T * k;
+    return ((size_t)((n + 3) & ~3) + small_lds_ints(n, El)) * 4;
+}
+
+bool route_group_fits(int T, int k, int E, int El) {
+    return T >= 1 && T <= kFusedTokens && E <= 1024 && route_group_lds_bytes(T, k, El) <= 65536;
+}
+
+template <int SLOTS>
+static void launch_route_group_slots(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
+                                     int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
+                                     int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                     int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr,
+                                     hipStream_t st) {
+    const size_t lds = route_group_lds_bytes(T, k, El);
+    auto kern = bf16 ? k_route_group_small<SLOTS, true> : k_route_group_small<SLOTS, false>;
+    kern<<<1, kScanThreads, lds, st>>>(logits, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, heavy_rows,
+                                       rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
+}
+
+hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
+                              int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
+                              int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
+    if (!route_group_fits(T, k, E, El)) return hipErrorInvalidValue;
+    const int slots = (E + 63) / 64;
+#define FMOE_RG(S)                                                                                                  \
+    launch_route_group_slots<S>(logits, bf16, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, heavy_rows, \
+                                rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy, hdr, st)
+    if (slots <= 1) FMOE_RG(1);
+    else if (slots <= 2) FMOE_RG(2);
+    else if (slots <= 4) FMOE_RG(4);
+    else if (slots <= 8) FMOE_RG(8);
+    else FMOE_RG(16);
+#undef FMOE_RG
     return hipGetLastError();
 }
 

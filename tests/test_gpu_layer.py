@@ -198,3 +198,33 @@ def test_every_tile_plan_matches_the_oracle(fp8):
                 assert st["tile_rows"] == tr and st["heavy_tiles"] > 0
                 err = row_rel_err(out.float().cpu().numpy(), ref)
                 assert err <= (FP8_TOL if fp8 else BF16_TOL), f"plan ({tr}, {s1}, {s2}): {err:.3e}"
+
+
+# Up to 16 tokens the forward routes and groups in one launch (wavefront t routes token t and
+# the same workgroup then groups the ids from LDS).  Its routing must equal the router
+# kernel's bit for bit, its grouping the grouping kernel's (same stats, identical output of
+# fmoe_experts on the same ids), and the output the oracle's; T = 17 takes the two-launch path.
+@pytest.mark.parametrize("T,H,I,E,k,ep,fp8,scoring,fp32", [
+    (1, 256, 128, 128, 8, 1, False, "softmax", False),
+    (3, 256, 256, 400, 6, 8, True, "sigmoid", False),    # E > 256: 8 slots per lane; rank 7 of 8
+    (16, 512, 256, 64, 8, 1, False, "sigmoid", True),    # fp32 logits
+    (16, 256, 128, 1000, 64, 2, False, "softmax", False),  # 16 slots, k = 64: 16 chunks of 64
+    (17, 256, 128, 64, 8, 1, False, "softmax", False),   # one past the fused limit
+])
+def test_small_batch_fused_router_and_grouping(T, H, I, E, k, ep, fp8, scoring, fp32):
+    announce(f"fused router+grouping T={T} H={H} I={I} E={E} k={k} ep={ep} fp8={fp8} {scoring} fp32={fp32}")
+    L = Layer(config=95, T=T, H=H, I=I, E=E, k=k, fp8=fp8, ep_size=ep, ep_rank=ep - 1, scoring=scoring)
+    lg = L.logits.clone()
+    lg[T // 2] = float("nan")  # one padding row
+    L.logits, L.logits_gpu = lg, (lg.float() if fp32 else lg).cuda()
+    ws = fm.workspace(L.shape)
+    out, ids, wts = L.forward(ws)
+    st_fwd = fm.fmoe_read_stats(ws)
+    sc = fm.FMOE_SOFTMAX if scoring == "softmax" else fm.FMOE_SIGMOID
+    ids_r, wts_r = fm.fmoe_router_topk(L.logits_gpu, k, sc, True)
+    assert torch.equal(ids, ids_r) and torch.equal(wts, wts_r)
+    assert ids[T // 2].tolist() == list(range(k))
+    out_e = fm.fmoe_experts(L.shape, L.x_gpu, ids, wts, L.w, ws=ws)
+    assert fm.fmoe_read_stats(ws) == st_fwd
+    assert torch.equal(out_e, out)
+    check_layer(L, n_sample=10 ** 6)
