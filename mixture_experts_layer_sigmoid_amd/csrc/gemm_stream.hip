@@ -19,6 +19,8 @@
 //
 // Every step issues the same loads (padding steps past the reduction end re-read the last
 // valid step, which hits in cache), so the compiler's static wait counts stay exact.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace fmoe {
@@ -56,14 +58,18 @@ struct StreamLds {
 
 __device__ __forceinline__ float silu_mul_s(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// a[i] for a lane-dependent i, as selects (an indexed read of a register array would go
-// through scratch memory)
+// a[i] for a runtime i, as a mask-and-or over the elements.  An indexed read of a register
+// array goes through scratch memory, and the compiler may fold a chain of selects over the
+// elements back into such a read (it did with 4 and 8 sub-blocks per tile); the masks keep
+// the array in registers.
 template <int N, typename T>
 __device__ __forceinline__ T pick(const T (&a)[N], int i) {
-    T r = a[0];
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit elements");
+    using U = typename std::conditional<sizeof(T) == 4, uint32_t, uint64_t>::type;
+    U r = 0;
 #pragma unroll
-    for (int j = 1; j < N; j++) r = i == j ? a[j] : r;
-    return r;
+    for (int j = 0; j < N; j++) r |= __builtin_bit_cast(U, a[j]) & (U)0 - (U)(i == j);
+    return __builtin_bit_cast(T, r);
 }
 
 // Where one task's operands live, for this lane.
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     constexpr int FPW = F / WV;  // pieces staged per wavefront
     constexpr int FEAT = 16 * WV;
     static_assert(F % WV == 0 && CS % D == 0, "chunk shape");
+    static_assert(!FP8 || CS * NS * 16 <= 64 * WV, "one thread per staged activation scale");
     __shared__ StreamLds<FP8, NS, CS> L;
 
     const int lane = lane_id();
@@ -195,15 +202,16 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             const int f = w * FPW + j;
             const int s = f / (NS * C::HALVES), sb = (f / C::HALVES) % NS, half = f % C::HALVES;
             const size_t step = (size_t)min(chunk * CS + s + c.soff, nsteps - 1);
-            xst[j] = *(const i32x4*)((const uint8_t*)g.A + xoff[sb] + step * (C::KSTEP * C::EB) + half * 16);
+            // sb depends on the wavefront index: picked, not an indexed register array
+            xst[j] = *(const i32x4*)((const uint8_t*)g.A + pick(xoff, sb) + step * (C::KSTEP * C::EB) + half * 16);
         }
         if constexpr (FP8) {
             // activation scales: thread t < CS*NS*16 takes step t / (NS*16) of row t % (NS*16),
-            // which is this lane's row (r16) of sub-block (lane / 16) % NS
+            // which is this lane's row (r16) of sub-block (t / 16) % NS
             const int t = threadIdx.x % (CS * NS * 16);
             const int s = t / (NS * 16);
             const int kb = min(chunk * CS + s + c.soff, nkb - 1);
-            ast = g.A_scale[(size_t)(pick(c.map, (lane >> 4) % NS) / topk) * nkb + kb];
+            ast = g.A_scale[(size_t)(pick(c.map, (t >> 4) % NS) / topk) * nkb + kb];
             // weight scales: thread t < NW*CS takes matrix t / CS, step t % CS
             const int u = threadIdx.x % (NW * CS);
             const int kw = min(chunk * CS + u % CS + c.soff, nkb - 1);

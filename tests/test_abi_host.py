@@ -139,7 +139,8 @@ def test_forward_planned_rejects_bad_plans_before_launching():
         return lib.fmoe_forward_planned(ctypes.byref(shape), P(0x100), P(0x100), 0, 0, 1, ctypes.byref(weights),
                                         P(0x300), None, None, P(0x400), fm.fmoe_workspace_bytes(shape), None,
                                         ctypes.byref(plan))
-    for bad in (fm.fmoe_plan(24, 0, 0), fm.fmoe_plan(0, 3, 0), fm.fmoe_plan(0, 0, 8), fm.fmoe_plan(-16, 1, 1)):
+    for bad in (fm.fmoe_plan(24, 0, 0), fm.fmoe_plan(0, 3, 0), fm.fmoe_plan(0, 0, 8), fm.fmoe_plan(-16, 1, 1),
+                fm.fmoe_plan(64, 1, 1), fm.fmoe_plan(48, 0, 0)):
         assert call(s, w, bad) == fm.FMOE_ERR_ARG
     # FP8 with a 65536-deep reduction: 32-row tiles would need 68 KB of activation scales in LDS
     s8 = fm.make_shape(16, 65536, 128, 8, 2, fp8=True)
