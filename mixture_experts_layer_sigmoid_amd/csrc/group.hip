@@ -327,6 +327,69 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
                 mtiles_heavy, hdr, lds);
 }
 
+// All three phases by one wavefront, for at most 64 assignments (one chunk) of which no expert
+// holds more than tile_rows (so every expert with rows is one light tile).  The results are
+// those of group_small: the chunk's counts are the expert totals, the exclusive scans over the
+// experts in ascending order give the offsets and the light tile slots, and each assignment
+// goes to its expert's offset plus its rank in the chunk.  cnt: El ints of LDS.
+__device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
+                           int rows_estimate, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm,
+                           MTile* __restrict__ mtiles, DevHeader* __restrict__ hdr, int* cnt) {
+    const int lane = lane_id();
+    int l, r, bad;
+    chunk_rank(ids, n, E, El, lo, 0, cnt, 1, cnt, &l, &r, &bad);  // cnt[e]: rows of expert e
+    // lane holds experts lane, lane + 64, ...: one wavefront scan per group of 64 experts
+    int run_rows = 0, run_tiles = 0, maxc = 0;
+    for (int e0 = 0; e0 < El; e0 += 64) {
+        const int e = e0 + lane;
+        const int c = e < El ? cnt[e] : 0;  // written by this lane in chunk_rank's copy
+        int sr = c, st = c > 0 ? 1 : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int yr = __shfl_up(sr, o, 64), yt = __shfl_up(st, o, 64);
+            if (lane >= o) {
+                sr += yr;
+                st += yt;
+            }
+        }
+        const int first = run_rows + sr - c, lfirst = run_tiles + st - (c > 0 ? 1 : 0);
+        if (e < El) {
+            counts[e] = c;
+            offsets[e] = first;
+            cnt[e] = first;
+            if (c > 0) {
+                MTile mt;
+                mt.expert = e;
+                mt.row0 = first;
+                mt.rows = c;
+                mt.group = 0;
+                mtiles[lfirst] = mt;
+            }
+        }
+        run_rows += __shfl(sr, 63, 64);
+        run_tiles += __shfl(st, 63, 64);
+        maxc = c > maxc ? c : maxc;
+    }
+    maxc = wave_max(maxc);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    chunk_scatter(lane, n, l, r, l >= 0 ? cnt[l] : 0, perm_src, inv_perm);
+    if (lane == 0) {
+        offsets[El] = run_rows;
+        hdr->m_tiles = run_tiles;
+        hdr->m_tiles_heavy = 0;
+        hdr->local_rows = run_rows;
+        hdr->max_rows = maxc;
+        hdr->empty_experts = El - run_tiles;
+        hdr->dropped = bad;
+        hdr->tile_rows = tile_rows;
+        hdr->heavy_rows = heavy_rows;
+        hdr->rows_estimate = rows_estimate;
+    }
+}
+
 // Router top-k and grouping in one launch for at most kFusedTokens tokens: wavefront t routes
 // token t (plain top-k, the router kernel's row code), writing ids and weights to global memory
 // and the ids to LDS as well; after one barrier the workgroup groups the ids from LDS.
@@ -345,6 +408,14 @@ __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
     const int w = threadIdx.x >> 6;
     if (w < T) topk_row<SLOTS, BF16_IN>(logits, w, E, k, scoring, renorm, 1, 1, ids, weights, ids_lds + w * k);
     __syncthreads();
+    // an expert holds at most T <= kFusedTokens <= tile_rows rows (distinct ids per token), so
+    // up to 64 assignments one wavefront groups them without workgroup barriers
+    if (n <= 64) {
+        if (w == 0)
+            group_wave(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src,
+                       inv_perm, mtiles, hdr, lds + ((n + 3) & ~3));
+        return;
+    }
     group_small(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm,
                 mtiles, mtiles_heavy, hdr, lds + ((n + 3) & ~3));
 }
@@ -429,7 +500,9 @@ static size_t route_group_lds_bytes(int T, int k, int El) {
     return ((size_t)((n + 3) & ~3) + small_lds_ints(n, El)) * 4;
 }
 
+// tile_rows >= 16 = kFusedTokens >= T, which the one-wavefront grouping relies on
 bool route_group_fits(int T, int k, int E, int El) {
+    static_assert(kFusedTokens <= 16, "every light tile holds at least 16 rows");
     return T >= 1 && T <= kFusedTokens && E <= 1024 && route_group_lds_bytes(T, k, El) <= 65536;
 }
 
