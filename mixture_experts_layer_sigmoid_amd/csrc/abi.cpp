@@ -12,7 +12,6 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
-#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -75,15 +74,17 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr) {
     p.n = (long long)p.T * p.k;
     long long est = (p.n + p.E - 1) / p.E;
     p.rows_estimate = (int)(est < 1 ? 1 : est);
-    // Largest row tile: the estimate plus three standard deviations of the per-expert count
-    // under uniform routing (about sqrt(estimate)), so a uniform batch rarely cuts an expert
-    // in two; heavier experts get more tiles on the device.  From 32 expected rows per expert
-    // on, most experts exceed a light tile anyway, and the tile-space sweep (bench.py
-    // --tile-sweep) measured the smallest light tile best there (every expert above 16 rows
-    // goes to the heavy-tile kernel): 270 against 304 us at T=512 of the 128-expert layer.
-    const double need = p.rows_estimate + 3.0 * std::sqrt((double)p.rows_estimate) + 1.0;
-    int tr = 16;
-    while (tr < need && tr < kLightRows) tr <<= 1;
+    // Largest row tile: 16 rows at one expected row per expert, 32 rows from two expected
+    // rows on (the estimate plus three standard deviations of the per-expert count under
+    // uniform routing, about sqrt(estimate), already exceeds 16 rows at 8).  The tile-space
+    // sweep (bench.py --tile-sweep) measured 32 rows at two expected rows as fast as 16 under
+    // uniform routing and faster under concentrated routing, where hot experts of up to 32 rows
+    // stay light tiles (T=32 of the 128-expert layer: 212 / 95 us against 214 / 108); at
+    // T <= 32 it also leaves no expert for the heavy-tile launches.  From 32 expected rows per
+    // expert on, most experts exceed a light tile anyway, and the sweep measured the smallest
+    // light tile best there (every expert above 16 rows goes to the heavy-tile kernel): 270
+    // against 304 us at T=512.
+    int tr = p.rows_estimate >= 2 ? kLightRows : 16;
     if (p.rows_estimate >= 32) tr = 16;
     // FP8 stages the tile's activation scales in LDS: keep them within 64 KB
     while (p.fp8 && tr > 16 && gemm_lds_bytes(true, p.H > p.I ? p.H : p.I, tr) > 65536) tr >>= 1;
@@ -93,14 +94,16 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr) {
     // expert under uniform routing) times the 16-feature blocks leave the GPU's 1024 SIMDs
     // with fewer than one wavefront each.  Otherwise the streaming kernel (no split), except
     // where the tile-space sweep measured a split of 2 faster (bf16 weights): the gate/up GEMM
-    // below 16 expected rows per expert (T=8: 133 -> 118 us, T=32: 225 -> 212 us), the down
-    // GEMM at one expected row (T=8: 118 -> 111 us); FP8 tiles stream best unsplit there.
+    // below 16 expected rows per expert (T=8: 133 -> 118 us, T=32: 225 -> 212 us) and from 32
+    // on, where the light tiles are the few experts left below 17 rows (T=512: equal under
+    // uniform routing, 311 -> 289 us under concentrated routing), and the down GEMM at one
+    // expected row (T=8: 118 -> 111 us); FP8 tiles stream best unsplit there.
     const long long local_rows = (p.n * p.El + p.E - 1) / p.E;
     const long long active = local_rows < p.El ? local_rows : p.El;
     auto pick_wk = [&](int N, bool gate_up) {
         const long long tasks = active * (N / 16);
         if (tasks < 1024) return 4;
-        if (!p.fp8 && (gate_up ? p.rows_estimate < 16 : p.rows_estimate <= 1)) return 2;
+        if (!p.fp8 && (gate_up ? p.rows_estimate < 16 || p.rows_estimate >= 32 : p.rows_estimate <= 1)) return 2;
         return tasks < 2048 ? 2 : 1;
     };
     p.wk1 = ov && ov->split_gate_up ? ov->split_gate_up : pick_wk(p.I, true);

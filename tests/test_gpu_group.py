@@ -30,9 +30,9 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
     est = max(1, -(-T * k // E))
     assert st["rows_estimate"] == est
     tr = st["tile_rows"]
-    # light tile: covers the estimate up to 32 rows; from 32 expected rows on, the smallest
-    # (every expert above 16 rows goes to the heavy-tile kernel)
-    assert tr in (16, 32) and (tr == 16 if est >= 32 else (tr >= est or tr == 32))
+    # light tile: 16 rows at one expected row, 32 from two on; from 32 expected rows on, the
+    # smallest again (every expert above 16 rows goes to the heavy-tile kernel)
+    assert tr == (16 if est == 1 or est >= 32 else 32)
     hr = st["heavy_rows"]
     assert hr == 256
     heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > tr))  # ceil(c / 256) equal tiles per heavy expert
