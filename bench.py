@@ -144,11 +144,12 @@ def pct(v, q):
     return s[i]
 
 
-def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None):
+def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None, every: int = 1):
     """warmup + steps timed calls, back to back; returns the wall time per call, per-call times
     from a start/end event pair (or, with `dominant`, the live duration of that stage from the
-    event pair around it), a separate untimed pass with every stage event, and the routing
-    counters of every batch."""
+    event pair around it, on every `every`-th timed call: each event record makes the stream
+    drain before the next kernel, so the other calls run as they do without instrumentation),
+    a separate untimed pass with every stage event, and the routing counters of every batch."""
     import torch
 
     import mixture_experts_layer_sigmoid_amd as fm
@@ -171,10 +172,12 @@ def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None):
         s = fm.STAGES.index(dominant)
         pair = (s, s + 1)
     ev = []
-    for _ in range(steps):
-        e = [None] * (NS + 1)
-        e[pair[0]] = HipEvent()
-        e[pair[1]] = HipEvent()
+    for i in range(steps):
+        e = None
+        if i % every == 0:
+            e = [None] * (NS + 1)
+            e[pair[0]] = HipEvent()
+            e[pair[1]] = HipEvent()
         ev.append(e)
 
     def call(j, events=None):
@@ -189,7 +192,7 @@ def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None):
         call(warmup + i, ev[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    pair_us = [ev[i][pair[0]].elapsed_time(ev[i][pair[1]]) * 1e3 for i in range(steps)]
+    pair_us = [ev[i][pair[0]].elapsed_time(ev[i][pair[1]]) * 1e3 for i in range(steps) if ev[i] is not None]
 
     # stage breakdown: a separate pass with every event (each record adds about a microsecond)
     full = [[HipEvent() for _ in range(NS + 1)] for _ in range(steps)]
@@ -377,6 +380,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-steps", type=int, default=12)
+    ap.add_argument("--roofline-every", type=int, default=4,
+                    help="time the dominant kernel with an event pair on every N-th timed step")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 256 MiB device copy (torch elementwise kernel): the reference launch "
                          "for scaling hardware byte counters")
@@ -424,7 +429,7 @@ def main():
     print(f"[bench] headline: {head.name}", file=sys.stderr, flush=True)
     # the gate/up GEMM streams two thirds of the touched weight bytes: the dominant kernel
     dom = "gemm1"
-    m = measure(head, args.steps, args.warmup, dominant=dom)
+    m = measure(head, args.steps, args.warmup, dominant=dom, every=max(1, args.roofline_every))
     hs = summarize(head, m)
     touched_bytes = m["touched"] * head.expert_bytes()
     value = touched_bytes / m["wall_s"] / 1e12
@@ -437,7 +442,8 @@ def main():
     roof = dict(kernel="k_grouped_gemm_stream (gate/up, SiLU-and-mul)", bound="hbm", achieved=round(achieved, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=traffic_from_profile(head.name, dom), algorithmic_bytes_per_launch=int(alg),
-                avg_launch_us=round(dom_us, 2), stage_breakdown_us={k: round(v, 2) for k, v in m["stage_us"].items()})
+                avg_launch_us=round(dom_us, 2), timed_launches=len(m["pair_us"]),
+                stage_breakdown_us={k: round(v, 2) for k, v in m["stage_us"].items()})
 
     sweep = [hs]
     if not args.no_sweep:
