@@ -134,8 +134,9 @@ class HipEvent:
         return f.value
 
     def __del__(self):
-        if self.cuda_event and HipEvent._hip is not None:
-            HipEvent._hip.hipEventDestroy(self.cuda_event)
+        hip = type(self)._hip  # not the module global, which is gone at interpreter exit
+        if self.cuda_event and hip is not None:
+            hip.hipEventDestroy(self.cuda_event)
 
 
 def pct(v, q):
