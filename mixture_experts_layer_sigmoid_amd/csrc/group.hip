@@ -11,7 +11,9 @@
 //
 // Small batches (at most 64 chunks) run all three phases in one workgroup and one launch;
 // larger ones run a counting launch over all chunks, a one-workgroup scan, and a scatter
-// launch, so the ballot work spreads over the whole GPU.
+// launch, so the ballot work spreads over the whole GPU.  Up to 16 tokens the forward routes
+// and groups in one launch (k_route_group_small); there, up to 64 assignments (one chunk) are
+// grouped by a single wavefront with wavefront scans, without workgroup barriers.
 //
 // Row tiles: the grouped GEMMs are cut per expert from the real row count, not from the
 // token count ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
