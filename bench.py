@@ -289,7 +289,8 @@ def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
 
 def tile_sweep(workloads, steps: int = 10) -> list:
     """Tile-space sweep: every tile plan the library can run (light tile rows 16/32 x gate/up
-    reduction split 1/2/4 x down split 1/2/4) against the host heuristic, per workload.  Each
+    reduction split 1/2/4 x down split 1/2/4 x light tiles per expert 1/8) against the host
+    heuristic, per workload.  Each
     variant: 2 warmup calls, then `steps` back-to-back calls timed between two events (GPU
     time per call), weights rotating over the workload's copies."""
     import torch
@@ -297,7 +298,8 @@ def tile_sweep(workloads, steps: int = 10) -> list:
     import mixture_experts_layer_sigmoid_amd as fm
 
     # the heuristic runs first and last (the faster of the two counts), after a warmup of its own
-    plans = [None] + [(tr, s1, s2) for tr in (16, 32) for s1 in (1, 2, 4) for s2 in (1, 2, 4)] + [None]
+    plans = [None] + [(tr, s1, s2, lt) for tr in (16, 32) for s1 in (1, 2, 4) for s2 in (1, 2, 4)
+                      for lt in (1, 8)] + [None]
     out = []
     for wl in workloads:
         print(f"[bench] tile sweep: {wl.name}", file=sys.stderr, flush=True)
@@ -327,7 +329,7 @@ def tile_sweep(workloads, steps: int = 10) -> list:
                 call(2 + j)
             b.record()
             torch.cuda.synchronize()
-            key = "heuristic" if plan is None else "tile %d, split %d/%d" % plan
+            key = "heuristic" if plan is None else "tile %d, split %d/%d, light tiles %d" % plan
             t = a.elapsed_time(b) * 1e3 / steps
             times[key] = min(t, times.get(key, t))
         best = min((v, k) for k, v in times.items() if k != "heuristic")
@@ -353,8 +355,11 @@ def sweep_workloads(B3, synth):
             work.append(Workload(f"bf16 H2048 I768 E128 top8, T={T}, {routing}", config=B3, T=T, H=2048, I=768,
                                  E=128, k=8, routing=routing))
     for T in (64, 128, 256):
-        work.append(Workload(f"fp8 w8a8 H2048 I768 E128 top8, T={T}, uniform", config=synth.FP8_LAYER,
-                             weight_config=B3, T=T, H=2048, I=768, E=128, k=8, fp8=True))
+        for routing in ("uniform", "concentrated"):
+            if T == 64 and routing == "concentrated":
+                continue
+            work.append(Workload(f"fp8 w8a8 H2048 I768 E128 top8, T={T}, {routing}", config=synth.FP8_LAYER,
+                                 weight_config=B3, T=T, H=2048, I=768, E=128, k=8, fp8=True, routing=routing))
     for routing in ("uniform", "concentrated"):
         work.append(Workload(f"fp8 shard H7168 I2048 top6 of 400 (ep 8, 50 local), T=288, {routing}",
                              config=synth.EP_SHARD, T=288, H=7168, I=2048, E=400, k=6, fp8=True, routing=routing,

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define FMOE_ABI_VERSION 1
+#define FMOE_ABI_VERSION 2
 
 /* Limits of this build (checked, FMOE_ERR_UNSUPPORTED beyond them). */
 #define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
@@ -177,9 +177,14 @@ int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int
  *                  into heavy tiles on the device)
  *   split_gate_up  wavefronts that split the reduction of a light tile in the gate/up GEMM:
  *                  1 (the streaming kernel), 2 or 4
- *   split_down     the same for the down GEMM */
+ *   split_down     the same for the down GEMM
+ *   light_tiles    light tiles one expert may take: 1 (experts above tile_rows rows are cut
+ *                  into heavy tiles) or 8 (experts of up to 8*tile_rows rows are cut into
+ *                  light tiles, and the heavy-tile launches are left out when no expert can
+ *                  hold more: at most T rows for router ids, T*top_k for caller ids); the
+ *                  heuristic takes 8 for FP8 weights and 1 for bf16 */
 typedef struct {
-    int32_t tile_rows, split_gate_up, split_down;
+    int32_t tile_rows, split_gate_up, split_down, light_tiles;
 } fmoe_plan;
 
 /* fmoe_forward with the nonzero fields of *plan (NULL: none) in place of the heuristic's

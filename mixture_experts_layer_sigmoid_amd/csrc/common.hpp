@@ -14,20 +14,21 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr float kE4M3Max = 448.0f;  // largest finite OCP E4M3FN magnitude
 constexpr int kMaxKBlocks = 512;    // 128-deep blocks of the reduction dimension (65536 / 128)
 constexpr int kLightRows = 32;      // largest row tile of the light GEMM kernel
+constexpr int kMaxLightPerExpert = 8;  // light tiles of one expert when heavy tiles are left out
 // largest row tile of the heavy GEMM kernel (4 groups of 64 rows)
 constexpr int heavy_max_rows(bool) { return 256; }
 
 // Workspace header written by the grouping kernel and read by later kernels and by
 // fmoe_read_stats.  Field order is part of the workspace format of this library only.
 struct DevHeader {
-    int32_t m_tiles;        // light row tiles (one per expert with 1..tile_rows rows)
+    int32_t m_tiles;        // light row tiles (of at most tile_rows rows)
     int32_t local_rows;     // R
     int32_t max_rows;       // largest per-expert count
     int32_t empty_experts;  // local experts with no row
     long long dropped;      // ids outside [0, E)
     int32_t tile_rows;      // largest rows per tile used to cut the experts
     int32_t rows_estimate;  // max(1, ceil(T*top_k/E)) of the host plan
-    int32_t m_tiles_heavy;  // heavy row tiles (experts with more than tile_rows rows)
+    int32_t m_tiles_heavy;  // heavy row tiles (experts with more than the light limit)
     int32_t heavy_rows;     // rows of a full heavy tile
     int32_t pad[6];
 };

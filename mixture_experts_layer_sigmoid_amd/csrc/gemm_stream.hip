@@ -19,6 +19,12 @@
 //
 // Every step issues the same loads (padding steps past the reduction end re-read the last
 // valid step, which hits in cache), so the compiler's static wait counts stay exact.
+//
+// FP8 gate/up may also quantise its output itself (the w8a8 scheme's per-row, per-128-column
+// activation scales): a workgroup of 8 wavefronts then holds all 128 features of one scale
+// group, the wavefronts combine their row maxima through LDS, and the codes and scales are
+// written in place of the fp32 activation, with the arithmetic of the quantisation kernel
+// (amax/448, IEEE reciprocal, fminf/fmaxf clamp, saturating conversion).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -84,7 +90,7 @@ struct Ctx {
     int soff;              // 0, or the step count for a padding context that re-reads the last step
 };
 
-template <bool GATED, bool FP8, bool OUT_F32, int NS, int D, int WV, int CS>
+template <bool GATED, bool FP8, int OUT, int NS, int D, int WV, int CS>
 __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     using C = SCfg<FP8>;
     using FT = typename C::T;
@@ -94,7 +100,9 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     constexpr int FEAT = 16 * WV;
     static_assert(F % WV == 0 && CS % D == 0, "chunk shape");
     static_assert(!FP8 || CS * NS * 16 <= 64 * WV, "one thread per staged activation scale");
+    static_assert(OUT != kOutE4M3 || (GATED && FP8 && FEAT == 128), "e4m3 output: one 128-feature group per workgroup");
     __shared__ StreamLds<FP8, NS, CS> L;
+    __shared__ float QM[OUT == kOutE4M3 ? NS * WV * 16 : 1];  // row maxima of each wavefront's 16 features
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -106,16 +114,21 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     const int nblocks = g.N / FEAT;
     const int mtc = *g.tile_count;
     // Task order.  Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups to the 8
-    // XCDs in turn), and every XCD has its own L2.  With at least 8 row tiles, tile m goes to
-    // XCD m % 8 and all its feature blocks run there, so the tile's activation rows are fetched
-    // into one L2 instead of up to eight; the workgroups of an XCD deal its tasks in turn.
+    // XCDs in turn), and every XCD has its own L2.  With at least 8 row tiles, each tile goes to
+    // one XCD and all its feature blocks run there, so the tile's activation rows are fetched
+    // into one L2 instead of up to eight; the workgroups of an XCD deal its tasks in turn.  The
+    // tiles are dealt to the XCDs in blocks of 8 consecutive tiles (tile m to XCD (m / 8) % 8)
+    // as long as every XCD gets a whole block, then one at a time: the light tiles of one
+    // expert are consecutive in the list, so an expert cut into several light tiles has them
+    // on one XCD, where they run at the same time and share the expert's weights in its L2.
     // With fewer tiles, tasks are dealt over all workgroups in order (spread over the XCDs).
     const int G = (int)gridDim.x, b = (int)blockIdx.x;
     const bool by_xcd = (G % 8 == 0) && mtc >= 8;
     const int xcd = b % 8, slot = b / 8, S = G / 8;
+    const int rounds = mtc / 64, rem = mtc - rounds * 64;  // whole rounds of 8 blocks of 8 tiles
     int ntasks;
     if (by_xcd) {
-        const int ntx = ((mtc - xcd + 7) / 8) * nblocks;  // tasks of this XCD
+        const int ntx = (rounds * 8 + (rem > xcd ? (rem - xcd + 7) / 8 : 0)) * nblocks;  // tasks of this XCD
         ntasks = ntx > slot ? (ntx - 1 - slot) / S + 1 : 0;
     } else {
         const int total = mtc * nblocks;
@@ -126,8 +139,8 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     auto task_at = [&](int i, int& mt, int& nb) {
         if (by_xcd) {
             const int j = slot + i * S;
-            const int q = j / nblocks;
-            mt = xcd + 8 * q;
+            const int q = j / nblocks;  // this XCD's q-th tile
+            mt = q < rounds * 8 ? (q >> 3) * 64 + xcd * 8 + (q & 7) : rounds * 64 + (q - rounds * 8) * 8 + xcd;
             nb = j - q * nblocks;
         } else {
             const int t = b + i * G;
@@ -263,6 +276,42 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     };
     // lane holds token column sb*16 + r16 and features n0 + 4*kg + i
     auto epilogue = [&](const CT& c, int n0) {
+        if constexpr (OUT == kOutE4M3) {
+            // every wavefront of the workgroup runs the same tasks, so all reach this barrier;
+            // QM is rewritten only after the next task's chunk barriers
+            float r[NS][4], am[NS];
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++) {
+                am[sb] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    r[sb][i] = silu_mul_s(acc[sb][0][i], acc[sb][NW - 1][i]);
+                    am[sb] = fmaxf(am[sb], fabsf(r[sb][i]));
+                }
+                am[sb] = fmaxf(am[sb], __shfl_xor(am[sb], 16, 64));
+                am[sb] = fmaxf(am[sb], __shfl_xor(am[sb], 32, 64));
+                if (kg == 0) QM[(sb * WV + w) * 16 + r16] = am[sb];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++) {
+                const int col = sb * 16 + r16;
+                if (col >= c.rows) continue;
+                float m = 0.0f;
+#pragma unroll
+                for (int v = 0; v < WV; v++) m = fmaxf(m, QM[(sb * WV + v) * 16 + r16]);
+                const float sc = (m == 0.0f) ? 1.0f : m / kE4M3Max;
+                const float inv = 1.0f / sc;
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) y[i] = fmaxf(fminf(r[sb][i] * inv, kE4M3Max), -kE4M3Max);
+                const size_t row = (size_t)(c.row0 + col);
+                *(uint32_t*)((uint8_t*)g.out + row * g.N + n0 + kg * 4) =
+                    f32x2_to_e4m3x2(y[0], y[1]) | (f32x2_to_e4m3x2(y[2], y[3]) << 16);
+                if (w == 0 && kg == 0) g.out_scale[row * (g.N >> 7) + (n0 >> 7)] = sc;
+            }
+            return;
+        }
 #pragma unroll
         for (int sb = 0; sb < NS; sb++) {
             const int col = sb * 16 + r16;
@@ -271,7 +320,7 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             float r[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_s(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
-            if (OUT_F32) {
+            if (OUT == kOutF32) {
                 *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
             } else {
                 uint2 pk;
@@ -336,17 +385,18 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
 }
 
 // wavefronts per workgroup: 8 for the down GEMM (its short reduction makes the tile's staged
-// activation rows a large share of the traffic: 128 features share them instead of 64)
-template <bool GATED>
-constexpr int stream_waves() { return GATED ? 4 : 8; }
+// activation rows a large share of the traffic: 128 features share them instead of 64) and
+// for a gate/up GEMM that quantises its output (one 128-feature scale group per workgroup)
+template <bool GATED, int OUT>
+constexpr int stream_waves() { return GATED && OUT != kOutE4M3 ? 4 : 8; }
 
-template <bool GATED, bool FP8, bool OUT_F32, int NS, int CS, int D>
+template <bool GATED, bool FP8, int OUT, int NS, int CS, int D>
 hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
-    constexpr int WV = stream_waves<GATED>();
+    constexpr int WV = stream_waves<GATED, OUT>();
     static int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV, CS>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT, NS, D, WV, CS>,
                                                           64 * WV, 0) != hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
@@ -355,7 +405,7 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
     grid = (grid + 7) / 8 * 8;  // a multiple of 8 for the per-XCD task order (extra workgroups exit)
-    k_grouped_gemm_stream<GATED, FP8, OUT_F32, NS, D, WV, CS><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
+    k_grouped_gemm_stream<GATED, FP8, OUT, NS, D, WV, CS><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -363,31 +413,39 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
 // 32-row tiles whose reduction is a multiple of 6 steps (768 deep: 6 steps) takes chunks of 6
 // with a ring of 3 instead, so no chunk is padded past the reduction end (a third of the
 // steps with chunks of 4); measured 10% faster there.
-template <bool GATED, bool FP8, bool OUT_F32>
+template <bool GATED, bool FP8, int OUT>
 hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, int cus, hipStream_t st) {
     constexpr int CS = SCfg<FP8>::CS, D = FP8 ? 4 : 8;
-    if (tile_rows == 16) return launch_stream<GATED, FP8, OUT_F32, 1, CS, D>(a, max_tiles, cus, st);
+    if (tile_rows == 16) return launch_stream<GATED, FP8, OUT, 1, CS, D>(a, max_tiles, cus, st);
     if (tile_rows == 32) {
         if constexpr (FP8 && !GATED) {
             const int nsteps = a.K / SCfg<FP8>::KSTEP;
-            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT_F32, 2, 6, 3>(a, max_tiles, cus, st);
+            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT, 2, 6, 3>(a, max_tiles, cus, st);
         }
-        return launch_stream<GATED, FP8, OUT_F32, 2, CS, D>(a, max_tiles, cus, st);
+        return launch_stream<GATED, FP8, OUT, 2, CS, D>(a, max_tiles, cus, st);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows,
+hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, int out_mode, const GemmArgs& a, int tile_rows,
                                       int max_tiles, int cus, hipStream_t st) {
     if (gated) {
-        if (fp8) return out_f32 ? launch_stream_rows<true, true, true>(a, tile_rows, max_tiles, cus, st)
-                                : launch_stream_rows<true, true, false>(a, tile_rows, max_tiles, cus, st);
-        return launch_stream_rows<true, false, false>(a, tile_rows, max_tiles, cus, st);
+        if (fp8) {
+            if (out_mode == kOutE4M3) {
+                if (a.N % 128 || !a.out_scale) return hipErrorInvalidValue;
+                return launch_stream_rows<true, true, kOutE4M3>(a, tile_rows, max_tiles, cus, st);
+            }
+            return out_mode == kOutF32 ? launch_stream_rows<true, true, kOutF32>(a, tile_rows, max_tiles, cus, st)
+                                       : launch_stream_rows<true, true, kOutBf16>(a, tile_rows, max_tiles, cus, st);
+        }
+        if (out_mode != kOutBf16) return hipErrorInvalidValue;
+        return launch_stream_rows<true, false, kOutBf16>(a, tile_rows, max_tiles, cus, st);
     }
-    if (fp8) return launch_stream_rows<false, true, false>(a, tile_rows, max_tiles, cus, st);
-    return launch_stream_rows<false, false, false>(a, tile_rows, max_tiles, cus, st);
+    if (out_mode != kOutBf16) return hipErrorInvalidValue;
+    if (fp8) return launch_stream_rows<false, true, kOutBf16>(a, tile_rows, max_tiles, cus, st);
+    return launch_stream_rows<false, false, kOutBf16>(a, tile_rows, max_tiles, cus, st);
 }
 
 }  // namespace fmoe

@@ -20,7 +20,9 @@
 // Selection", paragraphs 3-4): an expert with 1..tile_rows rows becomes one tile of the light
 // GEMM kernel, a heavier one (a hot expert of a concentrated routing, or any expert of a large
 // batch) is cut into tiles of at most 256 rows for the heavy kernel, rows spread as evenly as
-// 16-row steps allow.
+// 16-row steps allow.  When the host knows that no expert can exceed light_cap rows (a few
+// light tiles), experts above tile_rows are cut into several light tiles instead, and the
+// heavy-tile launches are left out.
 #include "launch.hpp"
 #include "router_row.hpp"
 
@@ -130,8 +132,8 @@ __device__ void block_scan4_max(const int (&v)[4], int mv, int* sh, int (&excl)[
 // the header.  Thread t works on expert e = t % El' and part p = t / El' of its chunks
 // (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
 // threads read consecutive experts of a chunk.
-__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int heavy_rows, int rows_estimate,
-                              long long dropped,
+__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int light_cap, int heavy_rows,
+                              int rows_estimate, long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
                               int* sh /* >= kScanShared ints */) {
@@ -164,10 +166,12 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
         total += v;
     }
     const int lead = (live && part == 0);
-    // an expert with 1..tile_rows rows is one light tile; a heavier one is cut into
-    // ceil(total / heavy_rows) tiles of equal size rounded up to 16 rows (the last one takes
-    // the rest), so the tiles of one expert carry about the same work
-    const bool heavy = total > tile_rows;
+    // an expert with 1..light_cap rows is cut into light tiles of tile_rows rows (the last one
+    // takes the rest); a heavier one is cut into ceil(total / heavy_rows) tiles of equal size
+    // rounded up to 16 rows (the last one takes the rest), so the tiles of one expert carry
+    // about the same work
+    const bool heavy = total > light_cap;
+    const int nlight = (total > 0 && !heavy) ? (total + tile_rows - 1) / tile_rows : 0;
     const int nheavy0 = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
     const int hrows = heavy ? min(heavy_rows, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
     const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0
@@ -176,7 +180,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
     // its lead thread), their totals, and the largest expert
     int first, lfirst, hfirst, max_rows;
     {
-        const int vals[4] = {lead ? total : 0, lead && total > 0 && !heavy, lead ? nheavy : 0, lead && total == 0};
+        const int vals[4] = {lead ? total : 0, lead ? nlight : 0, lead ? nheavy : 0, lead && total == 0};
         int ex[4], tot[4];
         block_scan4_max(vals, lead ? total : 0, sh, ex, tot, &max_rows);
         first = ex[0];
@@ -224,14 +228,14 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int h
             counts[e] = total;
             offsets[e] = first;
         }
-        // row tiles of expert e (heavy ones split over its P threads)
-        if (total > 0 && !heavy && part == 0) {
+        // row tiles of expert e (split over its P threads)
+        for (int j = part; j < nlight; j += P) {
             MTile mt;
             mt.expert = e;
-            mt.row0 = my_first;
-            mt.rows = total;
+            mt.row0 = my_first + j * tile_rows;
+            mt.rows = min(tile_rows, total - j * tile_rows);
             mt.group = 0;
-            mtiles[my_lfirst] = mt;
+            mtiles[my_lfirst + j] = mt;
         }
         if (heavy) {
             for (int j = part; j < nheavy; j += P) {
@@ -276,7 +280,7 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 // All three phases by one workgroup of kScanThreads.  ids may point to global memory or to
 // LDS (generic addressing); lds holds small_lds_ints(n, El) ints.
 __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, int El, int lo, int tile_rows,
-                                            int heavy_rows, int rows_estimate, int32_t* __restrict__ counts,
+                                            int light_cap, int heavy_rows, int rows_estimate, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                             int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                             MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr, int* lds) {
@@ -302,7 +306,8 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
     __syncthreads();
     long long dropped = 0;
     for (int c = 0; c < nchunk; c++) dropped += bads[c];
-    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles,
+                  mtiles_heavy, hdr, sh);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kSmallPerWave; j++) {
@@ -318,15 +323,16 @@ static size_t small_lds_ints(int n, int El) {
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
-                                                             int lo, int tile_rows, int heavy_rows, int rows_estimate,
+                                                             int lo, int tile_rows, int light_cap, int heavy_rows,
+                                                             int rows_estimate,
                                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
                                                              int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                                              MTile* __restrict__ mtiles_heavy,
                                                              DevHeader* __restrict__ hdr) {
     extern __shared__ int lds[];
-    group_small(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm, mtiles,
-                mtiles_heavy, hdr, lds);
+    group_small(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm,
+                mtiles, mtiles_heavy, hdr, lds);
 }
 
 // All three phases by one wavefront, for at most 64 assignments (one chunk) of which no expert
@@ -418,8 +424,8 @@ __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
                        inv_perm, mtiles, hdr, lds + ((n + 3) & ~3));
         return;
     }
-    group_small(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm,
-                mtiles, mtiles_heavy, hdr, lds + ((n + 3) & ~3));
+    group_small(ids_lds, n, E, El, lo, tile_rows, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src,
+                inv_perm, mtiles, mtiles_heavy, hdr, lds + ((n + 3) & ~3));
 }
 
 // ---------------------------------------------------------------- multi-workgroup path
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int heavy_rows, int rows_estimate,
+                                                            int light_cap, int heavy_rows, int rows_estimate,
                                                             const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
@@ -456,7 +462,8 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles, mtiles_heavy, hdr, sh);
+    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles,
+                  mtiles_heavy, hdr, sh);
 }
 
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
@@ -475,14 +482,15 @@ size_t group_scratch_bytes(long long n, int El) {
     return (size_t)(nchunk * El + nchunk) * sizeof(int);
 }
 
-hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
-                        int rows_estimate,
+hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
+                        int heavy_rows, int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
     const size_t lds = small_lds_ints(n, El) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
-        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts,
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate,
+                                                    counts,
                                                     offsets,
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
         return hipGetLastError();
@@ -490,7 +498,8 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
     int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, heavy_rows, rows_estimate, bad, counts,
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, bad,
+                                             counts,
                                              offsets, mtiles,
                                              mtiles_heavy, hdr);
     k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);

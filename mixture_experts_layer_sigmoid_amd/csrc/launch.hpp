@@ -15,7 +15,8 @@ struct GemmArgs {
     const float* S0;          // FP8: [El, N/128, K/128]
     const float* S1;
     int N, K;
-    void* out;                // [R, N] bf16, or fp32
+    void* out;                // [R, N] bf16, fp32, or e4m3 codes
+    float* out_scale;         // e4m3 output: [R, N/128] scales of the codes (the streaming kernel only)
     const MTile* mtiles;      // this kernel's row-tile list
     const int* tile_count;    // its length (written by the grouping kernel)
 };
@@ -31,8 +32,10 @@ hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
                               int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                               int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
-hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
-                        int rows_estimate,
+// light_cap >= tile_rows: experts with up to light_cap rows are cut into light tiles of tile_rows
+// rows, heavier ones into heavy tiles
+hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
+                        int heavy_rows, int rows_estimate,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int cols, uint8_t* q, float* s,
@@ -40,7 +43,10 @@ hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int co
 size_t gemm_lds_bytes(bool fp8, int K, int tile_rows);
 hipError_t launch_grouped_gemm(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows, int wk,
                                int max_tiles, int cus, hipStream_t st);
-hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int tile_rows,
+// Output of the streaming kernel: bf16, fp32, or (gated FP8 only) e4m3 codes with one fp32
+// scale per row and 128 features, quantised as launch_quant_rows does.
+enum StreamOut { kOutBf16 = 0, kOutF32 = 1, kOutE4M3 = 2 };
+hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, int out_mode, const GemmArgs& a, int tile_rows,
                                       int max_tiles, int cus, hipStream_t st);
 // heavy row tiles (up to 256 rows) with both operands tiled through LDS
 hipError_t launch_grouped_gemm_tiled(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,

@@ -28,9 +28,9 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = fm.load_library()
-    assert fm.fmoe_abi_version() == 1
+    assert fm.fmoe_abi_version() == 2
     text = open(HEADER).read()
-    assert "#define FMOE_ABI_VERSION 1" in text
+    assert "#define FMOE_ABI_VERSION 2" in text
     for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")]:
         assert word in lib.fmoe_status_string(code)
 
@@ -140,7 +140,8 @@ def test_forward_planned_rejects_bad_plans_before_launching():
                                         P(0x300), None, None, P(0x400), fm.fmoe_workspace_bytes(shape), None,
                                         ctypes.byref(plan))
     for bad in (fm.fmoe_plan(24, 0, 0), fm.fmoe_plan(0, 3, 0), fm.fmoe_plan(0, 0, 8), fm.fmoe_plan(-16, 1, 1),
-                fm.fmoe_plan(64, 1, 1), fm.fmoe_plan(48, 0, 0)):
+                fm.fmoe_plan(64, 1, 1), fm.fmoe_plan(48, 0, 0), fm.fmoe_plan(0, 0, 0, 2), fm.fmoe_plan(0, 0, 0, -1),
+                fm.fmoe_plan(16, 1, 1, 16)):
         assert call(s, w, bad) == fm.FMOE_ERR_ARG
     # FP8 with a 65536-deep reduction: 32-row tiles would need 68 KB of activation scales in LDS
     s8 = fm.make_shape(16, 65536, 128, 8, 2, fp8=True)

@@ -12,9 +12,9 @@ from gpu_common import announce
 pytestmark = pytest.mark.gpu
 
 
-def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
+def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128, fp8=False):
     T, k = ids.shape
-    shape = fm.make_shape(T, H, I, E, k, ep_size, ep_rank)
+    shape = fm.make_shape(T, H, I, E, k, ep_size, ep_rank, fp8=fp8)
     r = fm.fmoe_route_permute(shape, torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda())
     ref = oracle.route_permute(ids, E, ep_size, ep_rank)
     R = int(ref["offsets"][-1])
@@ -35,8 +35,11 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
     assert tr == (16 if est == 1 or est >= 32 else 32)
     hr = st["heavy_rows"]
     assert hr == 256
-    heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > tr))  # ceil(c / 256) equal tiles per heavy expert
-    light = int(sum(1 for c in ref["counts"] if 0 < c <= tr))
+    # FP8: caller ids may repeat, so an expert can hold up to T*k rows; when that fits 8 light
+    # tiles, every expert is cut into light tiles of tr rows and there are no heavy tiles
+    cap = 8 * tr if fp8 and T * k <= 8 * tr else tr
+    heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > cap))  # ceil(c / 256) equal tiles per heavy expert
+    light = int(sum(-(-c // tr) for c in ref["counts"] if 0 < c <= cap))
     assert st["heavy_tiles"] == heavy
     assert st["m_tiles"] == light + heavy
     return r, ref
@@ -47,11 +50,12 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128):
     (288, 6, 400, 8, 0), (288, 6, 400, 8, 5), (513, 8, 64, 4, 3), (4096, 8, 128, 1, 0), (2000, 2, 1024, 1, 0),
     (512, 8, 128, 1, 0), (1024, 4, 16, 1, 0), (1040, 4, 16, 2, 1),  # 64 chunks (one launch), 65 chunks
 ])
-def test_group_random_ids_with_duplicates(T, k, E, ep_size, ep_rank):
-    announce(f"group T={T} k={k} E={E} ep={ep_size}/{ep_rank}")
+@pytest.mark.parametrize("fp8", [False, True])  # FP8: several light tiles per expert where they bound it
+def test_group_random_ids_with_duplicates(T, k, E, ep_size, ep_rank, fp8):
+    announce(f"group T={T} k={k} E={E} ep={ep_size}/{ep_rank} fp8={fp8}")
     g = np.random.default_rng(T * 7 + E)
     ids = g.integers(0, E, (T, k)).astype(np.int32)  # repeated ids in a token are legal
-    check_group(ids, E, ep_size, ep_rank)
+    check_group(ids, E, ep_size, ep_rank, fp8=fp8)
 
 
 def test_group_router_ids_full_sizes():

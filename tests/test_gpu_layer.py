@@ -43,7 +43,8 @@ def test_bf16_layer_small(T, H, I, E, k, routing, scoring):
 
 
 @pytest.mark.parametrize("T,H,I,E,k,ep", [(50, 512, 256, 8, 2, 1), (40, 256, 384, 16, 6, 2), (200, 256, 256, 4, 2, 1),
-                                          (20, 128, 128, 4, 2, 1)])  # one 128-deep block: idle split-K waves
+                                          (20, 128, 128, 4, 2, 1),  # one 128-deep block: idle split-K waves
+                                          (120, 256, 256, 8, 2, 1)])  # experts in 1-2 light tiles, no heavy tiles
 def test_fp8_layer_small(T, H, I, E, k, ep):
     announce(f"fp8 layer T={T} H={H} I={I} E={E} k={k} ep={ep}")
     L = Layer(config=91, T=T, H=H, I=I, E=E, k=k, fp8=True, ep_size=ep, ep_rank=ep - 1)
@@ -65,6 +66,24 @@ def test_layer_streaming_kernel_shapes(T, H, I, E, k, ep, fp8):
     L = Layer(config=94, T=T, H=H, I=I, E=E, k=k, fp8=fp8, ep_size=ep, ep_rank=ep - 1)
     L.plan = fm.fmoe_plan(0, 1, 1)
     check_layer(L, n_sample=10 ** 6)
+
+
+# Experts cut into several light tiles (up to 8 per expert, the heavy-tile launches left out):
+# hot experts of a concentrated routing span two or more 32-row tiles (at most T=120 rows),
+# ragged last tiles; FP8 also quantises the activation in the gate/up kernel.
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("routing", ["uniform", "concentrated"])
+def test_layer_multi_light_tiles(fp8, routing):
+    announce(f"several light tiles per expert, fp8={fp8} {routing}")
+    L = Layer(config=95, T=120, H=256, I=384, E=16, k=4, fp8=fp8, routing=routing)
+    L.plan = fm.fmoe_plan(32, 1, 1, 8)
+    check_layer(L, n_sample=10 ** 6)
+    ws = fm.workspace(L.shape)
+    L.forward(ws)
+    st = fm.fmoe_read_stats(ws)
+    assert st["heavy_tiles"] == 0 and st["m_tiles"] >= -(-st["max_rows"] // 32)
+    if routing == "concentrated":
+        assert st["max_rows"] > 32  # hot experts take two light tiles or more
 
 
 @pytest.mark.parametrize("T", [1, 8, 32, 128, 256, 512, 1024, 4096])
@@ -160,7 +179,7 @@ def test_forward_is_deterministic_and_matches_experts():
 
 def test_profiled_forward_and_hip_graph_replays_match_eager():
     announce("profiled forward and HIP graph capture/replays vs eager (concentrated, heavy tiles)")
-    L = Layer(config=synth.BF16_LAYER, T=256, H=2048, I=768, E=128, k=8, routing="concentrated")
+    L = Layer(config=synth.BF16_LAYER, T=512, H=2048, I=768, E=128, k=8, routing="concentrated")
     ws = fm.workspace(L.shape)
     eager = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws)
     assert fm.fmoe_read_stats(ws)["heavy_tiles"] > 0
@@ -182,7 +201,7 @@ def test_profiled_forward_and_hip_graph_replays_match_eager():
 
 @pytest.mark.parametrize("fp8", [False, True])
 def test_every_tile_plan_matches_the_oracle(fp8):
-    announce(f"all 18 tile plans (tile rows x gate/up split x down split), concentrated, fp8={fp8}")
+    announce(f"all 36 tile plans (tile rows x gate/up split x down split x light tiles), concentrated, fp8={fp8}")
     T, H, I, E, k = 130, 384, 256, 32, 8
     L = Layer(config=101, T=T, H=H, I=I, E=E, k=k, fp8=fp8, routing="concentrated")
     ids_ref, w_ref = L.oracle_routing()
@@ -191,13 +210,17 @@ def test_every_tile_plan_matches_the_oracle(fp8):
     for tr in (16, 32):
         for s1 in (1, 2, 4):
             for s2 in (1, 2, 4):
-                out, ids, _ = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, return_routing=True,
-                                              plan=fm.fmoe_plan(tr, s1, s2))
-                assert np.array_equal(ids.cpu().numpy(), ids_ref)
-                st = fm.fmoe_read_stats(ws)
-                assert st["tile_rows"] == tr and st["heavy_tiles"] > 0
-                err = row_rel_err(out.float().cpu().numpy(), ref)
-                assert err <= (FP8_TOL if fp8 else BF16_TOL), f"plan ({tr}, {s1}, {s2}): {err:.3e}"
+                for lt in (1, 8):
+                    out, ids, _ = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, return_routing=True,
+                                                  plan=fm.fmoe_plan(tr, s1, s2, lt))
+                    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+                    st = fm.fmoe_read_stats(ws)
+                    # an expert holds at most T = 130 rows: 8 light tiles of 32 rows cover it
+                    light_only = lt == 8 and T <= 8 * tr
+                    assert st["tile_rows"] == tr and (st["heavy_tiles"] == 0) == light_only
+                    assert st["m_tiles"] - st["heavy_tiles"] >= (st["max_rows"] + tr - 1) // tr
+                    err = row_rel_err(out.float().cpu().numpy(), ref)
+                    assert err <= (FP8_TOL if fp8 else BF16_TOL), f"plan ({tr}, {s1}, {s2}, {lt}): {err:.3e}"
 
 
 # Up to 16 tokens the forward routes and groups in one launch (wavefront t routes token t and
