@@ -207,9 +207,10 @@ void record(void* const* ev, int i, hipStream_t st) {
 }
 
 // Grouping, expert GEMMs and combine for routing already in ids/wts (device pointers).
-// grouped: the fused router + grouping launch has already written the grouping.
+// grouped: the fused router + grouping launch has already written the grouping; x_quantised:
+// the router launch has already written the FP8 codes and scales of x.
 int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* wts, const fmoe_weights* w, void* out,
-                char* ws, hipStream_t st, void* const* ev, bool grouped = false) {
+                char* ws, hipStream_t st, void* const* ev, bool grouped = false, bool x_quantised = false) {
     const Layout& L = p.L;
     DevHeader* hdr = (DevHeader*)(ws + L.hdr);
     int32_t* perm = (int32_t*)(ws + L.perm);
@@ -230,7 +231,8 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     const bool fused_quant_h = p.fp8 && !heavy_possible && p.wk1 == 1;
 
     record(ev, FMOE_STAGE_QUANT_X, st);
-    if (p.fp8) FMOE_TRY(launch_quant_rows(x, true, p.T, p.H, (uint8_t*)(ws + L.xq), (float*)(ws + L.xs), nullptr, st));
+    if (p.fp8 && !x_quantised)
+        FMOE_TRY(launch_quant_rows(x, true, p.T, p.H, (uint8_t*)(ws + L.xq), (float*)(ws + L.xs), nullptr, st));
 
     record(ev, FMOE_STAGE_GEMM1, st);
     GemmArgs g1;
@@ -325,17 +327,20 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
     float* wts = wts_out ? wts_out : (float*)(wsb + p.L.wts);
     record(ev, FMOE_STAGE_ROUTER, st);
     const bool bf16 = logits_dtype == FMOE_BF16;
+    // FP8: the router launch quantises x as well (one token row per wavefront)
+    const XQuant xq = {x, p.H, (uint8_t*)(wsb + p.L.xq), (float*)(wsb + p.L.xs)};
+    const XQuant* xqp = p.fp8 ? &xq : nullptr;
     if (route_group_fits((int)p.T, p.k, p.E, p.El)) {  // small batch: router and grouping in one launch
         const Layout& L = p.L;
         MTile* mtiles = (MTile*)(wsb + L.mtiles);
         FMOE_TRY(launch_route_group(logits, bf16, (int)p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, p.El, p.lo,
                                     p.tile_rows, p.heavy_rows, p.rows_estimate, (int32_t*)(wsb + L.counts),
                                     (int32_t*)(wsb + L.offsets), (int32_t*)(wsb + L.perm), (int32_t*)(wsb + L.inv),
-                                    mtiles, mtiles + p.max_light, (DevHeader*)(wsb + L.hdr), st));
-        return run_experts(p, x, ids, wts, w, out, wsb, st, ev, true);
+                                    mtiles, mtiles + p.max_light, (DevHeader*)(wsb + L.hdr), st, xqp));
+        return run_experts(p, x, ids, wts, w, out, wsb, st, ev, true, p.fp8);
     }
-    FMOE_TRY(launch_router_topk(logits, bf16, p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, st));
-    return run_experts(p, x, ids, wts, w, out, wsb, st, ev);
+    FMOE_TRY(launch_router_topk(logits, bf16, p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, st, 1, 1, xqp));
+    return run_experts(p, x, ids, wts, w, out, wsb, st, ev, false, p.fp8);
 }
 
 }  // namespace

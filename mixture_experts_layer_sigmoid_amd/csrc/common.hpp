@@ -60,6 +60,34 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// One group of 128 values quantised by one wavefront, two values per lane (a, b: elements 2l
+// and 2l+1 of lane l): amax = max|v| (NaN ignored, as fmaxf does), s = amax/448 (1 for an
+// all-zero group), inv = 1/s, code = e4m3(clamp(v*inv, +-448)).  The clamp uses fminf/fmaxf,
+// so a NaN value becomes +448.  IEEE division (no fast-math), so codes and scales are
+// reproducible bit for bit.  q2: this lane's two code bytes; s: the group's scale.
+__device__ __forceinline__ void quant_group_wave(float a, float b, uint8_t* q2, float* s) {
+    float am = fmaxf(fmaxf(0.0f, fabsf(a)), fabsf(b));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    const float sc = (am == 0.0f) ? 1.0f : am / kE4M3Max;
+    const float inv = 1.0f / sc;
+    const float ya = fmaxf(fminf(a * inv, kE4M3Max), -kE4M3Max);
+    const float yb = fmaxf(fminf(b * inv, kE4M3Max), -kE4M3Max);
+    *(uint16_t*)q2 = (uint16_t)f32x2_to_e4m3x2(ya, yb);
+    if (lane_id() == 0) *s = sc;
+}
+
+// Group g (row g / (cols/128), column group g % (cols/128)) of a bf16 matrix with `cols`
+// columns (a multiple of 128), quantised by one wavefront; its scale goes to s[g].
+__device__ __forceinline__ void quant_group_bf16_wave(const uint16_t* __restrict__ x, int cols, long long g,
+                                                      uint8_t* __restrict__ q, float* __restrict__ s) {
+    const int G = cols >> 7;
+    const long long row = g / G;
+    const size_t base = (size_t)row * cols + (size_t)(g - row * G) * 128 + lane_id() * 2;
+    const uint32_t two = *(const uint32_t*)(x + base);
+    quant_group_wave(bf16_to_f32((uint16_t)(two & 0xffffu)), bf16_to_f32((uint16_t)(two >> 16)), q + base, s + g);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll

@@ -403,17 +403,22 @@ __device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int
 // and the ids to LDS as well; after one barrier the workgroup groups the ids from LDS.
 constexpr int kFusedTokens = kScanThreads / 64;
 
-template <int SLOTS, bool BF16_IN>
+template <int SLOTS, bool BF16_IN, bool QX>
 __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
     const void* __restrict__ logits, int T, int E, int k, int scoring, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ weights, int El, int lo, int tile_rows, int heavy_rows, int rows_estimate,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
-    DevHeader* __restrict__ hdr) {
+    DevHeader* __restrict__ hdr, XQuant xq) {
     extern __shared__ int lds[];
     const int n = T * k;
     int* ids_lds = lds;  // [n], padded to 4 ints
     const int w = threadIdx.x >> 6;
+    if (QX && blockIdx.x > 0) {  // FP8: workgroups 1.. quantise x, one 128-column group per wavefront
+        const long long g = (long long)(blockIdx.x - 1) * (kScanThreads / 64) + w;
+        if (g < (long long)T * (xq.H >> 7)) quant_group_bf16_wave((const uint16_t*)xq.x, xq.H, g, xq.q, xq.s);
+        return;
+    }
     if (w < T) topk_row<SLOTS, BF16_IN>(logits, w, E, k, scoring, renorm, 1, 1, ids, weights, ids_lds + w * k);
     __syncthreads();
     // an expert holds at most T <= kFusedTokens <= tile_rows rows (distinct ids per token), so
@@ -522,22 +527,29 @@ static void launch_route_group_slots(const void* logits, bool bf16, int T, int E
                                      int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
                                      int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                                      int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr,
-                                     hipStream_t st) {
+                                     hipStream_t st, const XQuant* xq) {
     const size_t lds = route_group_lds_bytes(T, k, El);
-    auto kern = bf16 ? k_route_group_small<SLOTS, true> : k_route_group_small<SLOTS, false>;
-    kern<<<1, kScanThreads, lds, st>>>(logits, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, heavy_rows,
-                                       rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
+    const XQuant none = {nullptr, 0, nullptr, nullptr};
+    auto kern = bf16 ? (xq ? k_route_group_small<SLOTS, true, true> : k_route_group_small<SLOTS, true, false>)
+                     : (xq ? k_route_group_small<SLOTS, false, true> : k_route_group_small<SLOTS, false, false>);
+    // workgroup 0 routes and groups; FP8: one more workgroup per 16 groups of x to quantise
+    const unsigned blocks = xq ? 1 + (unsigned)((T * (xq->H / 128) + kScanThreads / 64 - 1) / (kScanThreads / 64)) : 1;
+    kern<<<blocks, kScanThreads, lds, st>>>(logits, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, heavy_rows,
+                                       rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy, hdr,
+                                       xq ? *xq : none);
 }
 
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
                               int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                              int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
+                              int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st,
+                              const XQuant* xq) {
     if (!route_group_fits(T, k, E, El)) return hipErrorInvalidValue;
+    if (xq && (!xq->x || !xq->q || !xq->s || xq->H <= 0 || xq->H % 128)) return hipErrorInvalidValue;
     const int slots = (E + 63) / 64;
 #define FMOE_RG(S)                                                                                                  \
     launch_route_group_slots<S>(logits, bf16, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, heavy_rows, \
-                                rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy, hdr, st)
+                                rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy, hdr, st, xq)
     if (slots <= 1) FMOE_RG(1);
     else if (slots <= 2) FMOE_RG(2);
     else if (slots <= 4) FMOE_RG(4);

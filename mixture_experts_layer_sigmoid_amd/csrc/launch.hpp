@@ -21,17 +21,29 @@ struct GemmArgs {
     const int* tile_count;    // its length (written by the grouping kernel)
 };
 
+// FP8 layers: the router launch also quantises x ([T, H] bf16) to e4m3 codes q [T, H] and scales
+// s [T, H/128] (the code of launch_quant_rows): extra workgroups of the same launch take one
+// 128-column group per wavefront, beside the routing workgroups.
+struct XQuant {
+    const void* x;
+    int H;
+    uint8_t* q;
+    float* s;
+};
+
 hipError_t launch_router_logits(const void* x, const void* w, int T, int H, int E, float* logits, hipStream_t st);
 // n_group groups of E/n_group experts, topk_group of them kept (n_group = topk_group = 1: plain top-k)
 hipError_t launch_router_topk(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
-                              int32_t* ids, float* weights, hipStream_t st, int n_group = 1, int topk_group = 1);
+                              int32_t* ids, float* weights, hipStream_t st, int n_group = 1, int topk_group = 1,
+                              const XQuant* xq = nullptr);
 size_t group_scratch_bytes(long long n, int El);
 // Router top-k (plain) and grouping in one launch, for small T: route_group_fits says when.
 bool route_group_fits(int T, int k, int E, int El);
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
                               int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                              int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
+                              int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st,
+                              const XQuant* xq = nullptr);
 // light_cap >= tile_rows: experts with up to light_cap rows are cut into light tiles of tile_rows
 // rows, heavier ones into heavy tiles
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,

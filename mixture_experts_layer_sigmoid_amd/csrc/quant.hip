@@ -2,12 +2,13 @@
 // "Lab notes #6: We tuned vLLM's MoE kernels on an H100 ...", intro: fp8_w8a8 with
 // block_shape [128,128]; activation scales per token and 128-column group, fp32).
 //
-// One wavefront per group of 128 values, two per lane: amax = max|x| (NaN ignored, as
-// fmaxf does), s = amax/448 (1 for an all-zero group), inv = 1/s, code = e4m3(clamp(x*inv,
-// +-448)).  The clamp uses fminf/fmaxf, so a NaN input becomes +448: the saturating FP8
-// conversion that "PR #39593: [Bug]: Fix FlashInfer CUTLASS BF16 + CUDA graphs IMA" (Root
-// cause) calls a NaN firewall.  IEEE division (no fast-math), so codes and scales are
-// reproducible bit for bit.
+// One wavefront per group of 128 values, two per lane (quant_group_wave): amax = max|x| (NaN
+// ignored, as fmaxf does), s = amax/448 (1 for an all-zero group), inv = 1/s, code =
+// e4m3(clamp(x*inv, +-448)).  The clamp uses fminf/fmaxf, so a NaN input becomes +448: the
+// saturating FP8 conversion that "PR #39593: [Bug]: Fix FlashInfer CUTLASS BF16 + CUDA graphs
+// IMA" (Root cause) calls a NaN firewall.  IEEE division (no fast-math), so codes and scales
+// are reproducible bit for bit.  The forward quantises x in the router launch instead, with the
+// same per-group code.
 #include "launch.hpp"
 
 namespace fmoe {
@@ -36,15 +37,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         a = two.x;
         b = two.y;
     }
-    float am = fmaxf(fmaxf(0.0f, fabsf(a)), fabsf(b));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    const float sc = (am == 0.0f) ? 1.0f : am / kE4M3Max;
-    const float inv = 1.0f / sc;
-    const float ya = fmaxf(fminf(a * inv, kE4M3Max), -kE4M3Max);
-    const float yb = fmaxf(fminf(b * inv, kE4M3Max), -kE4M3Max);
-    *(uint16_t*)(q + base) = (uint16_t)f32x2_to_e4m3x2(ya, yb);
-    if (lane == 0) s[g] = sc;
+    quant_group_wave(a, b, q + base, s + g);
 }
 
 hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int cols, uint8_t* q, float* s,

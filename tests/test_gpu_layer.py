@@ -140,6 +140,37 @@ def test_experts_all_tokens_one_expert_duplicates_and_dropped_ids():
         assert st["dropped_ids"] == int(((ids < 0) | (ids >= E)).sum())
 
 
+# The forward quantises x inside its router launch (the fused router + grouping launch up to 16
+# tokens, the router kernel above); fmoe_experts runs the separate quantisation kernel.  Same
+# codes and the same tile plan give the same output bits.
+@pytest.mark.parametrize("T", [12, 100])
+def test_fp8_forward_quantises_x_in_the_router_launch(T):
+    announce(f"fp8 forward (x quantised by the router launch) == experts (quantisation kernel), T={T}")
+    L = Layer(config=96, T=T, H=384, I=256, E=8, k=2, fp8=True)
+    out, ids, wts = L.forward()
+    out2 = fm.fmoe_experts(L.shape, L.x_gpu, ids, wts, L.w)
+    assert torch.equal(out, out2)
+    check_layer(L, n_sample=10 ** 6)
+
+
+@pytest.mark.parametrize("T", [12, 40])
+def test_fp8_nan_activation_rows_stay_in_their_tokens(T):
+    announce(f"fp8 layer with NaN rows of x, T={T}")
+    L = Layer(config=97, T=T, H=256, I=256, E=8, k=2, fp8=True)
+    bad = [1, T - 2]
+    x = L.x.clone()
+    x[bad] = float("nan")
+    L.x, L.x_gpu = x, x.cuda()
+    out, ids, _ = L.forward()
+    ids_ref, w_ref = L.oracle_routing()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    others = np.array([t for t in range(T) if t not in bad], np.int32)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()  # the quantiser clamps NaN to +448 (a finite code)
+    ref = L.oracle_tokens(ids_ref, w_ref, others)
+    assert row_rel_err(got[others], ref) <= FP8_TOL
+
+
 def test_nan_logit_rows_give_distinct_experts_and_finite_output():
     announce("layer with all-NaN logit rows (padding tokens)")
     L = Layer(config=92, T=40, H=256, I=256, E=16, k=4)
