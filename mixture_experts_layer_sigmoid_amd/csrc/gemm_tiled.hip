@@ -8,8 +8,10 @@
 // kernel is built around the matrix cores rather than the weight stream.
 //
 // Shape: one workgroup of 8 wavefronts computes a tile of up to 256 rows times 128 weight
-// columns (gate/up: 64 features of each matrix, so SiLU-and-mul happens in registers); the
-// wavefronts form a 4 x 2 grid, each owning 64 rows x 64 columns (16 accumulators of 16 x 16).
+// columns (gate/up: 64 features of each matrix, so SiLU-and-mul happens in registers).  The
+// tile's rows are staged in NA groups of 64 (NA = 1..4); the wavefronts form a 4 x 2 grid, each
+// owning 16*NA rows x 64 columns (4*NA accumulators of 16 x 16), so all 8 wavefronts, and all
+// four SIMDs equally, carry MFMA work whatever the tile's size.
 // Every 128-byte slice of the reduction (64 bf16 or 128 e4m3 per row) is one stage: the
 // activation rows (gathered through the row map) and the weight rows are copied straight from
 // global memory into LDS by direct global-to-LDS loads, three stages deep, so two stages are in
@@ -18,8 +20,8 @@
 // groups.  Each buffer is a separate LDS array and every wait is an explicit count of the loads
 // that must have landed, so the compiler never has to wait for loads into another buffer.
 //
-// Per stage and wavefront: 8 fragment reads (16 KB) feed 32 MFMAs of 16x16x32 (bf16), or
-// 4 + 4 double-width reads feed 16 MFMAs of 16x16x128 (FP8, one per 128-deep scale block,
+// Per stage and wavefront (NA = 4): 8 fragment reads (16 KB) feed 32 MFMAs of 16x16x32 (bf16),
+// or 4 + 4 double-width reads feed 16 MFMAs of 16x16x128 (FP8, one per 128-deep scale block,
 // whose product is added times weight scale x activation scale).
 //
 // Work order: the tasks (row tile, column block) of one expert run column block first, then
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = w >> 1, wn = w & 1;  // row group (64 rows) and column group (64 columns)
+    const int wm = w >> 1, wn = w & 1;  // row group (16*NA rows) and column group (64 columns)
     const int r16 = lane & 15, kg = lane >> 4;
     const int K = g.K;
     const size_t rowbytes = (size_t)K * (FP8 ? 1 : 2);
@@ -173,15 +175,15 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                 }
             };
 
-            f32x4 acc[4][4];
+            f32x4 acc[NA][4];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int i = 0; i < NA; i++)
 #pragma unroll
                 for (int c = 0; c < 4; c++) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
             // weight rows of column block c of this wavefront (gate/up: c = 0,1 gate, 2,3 up)
             auto wcol = [&](int c) { return GATED ? (c >> 1) * 64 + wn * 32 + (c & 1) * 16 : wn * 64 + c * 16; };
-            const bool active = wm < NA;  // this wavefront's 64 rows hold some of the tile
+            const int rb0 = wm * 16 * NA;  // first tile row of this wavefront
             // FP8 weight scales of the block: one per matrix and 128-deep block
             const int fb = GATED ? nb / 2 : nb;
             const size_t sidx = ((size_t)expert * (g.N / 128) + fb) * nkb128;
@@ -190,18 +192,17 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                 constexpr int B = decltype(Bc)::value;
                 const i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
                 const i32x4* W = B == 0 ? W0 : B == 1 ? W1 : W2;
-                if (!active) return;
                 if constexpr (!FP8) {
 #pragma unroll
                     for (int q = 0; q < 2; q++) {
-                        bf16x8 xa[4], wb[4];
+                        bf16x8 xa[NA], wb[4];
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            xa[i] = __builtin_bit_cast(bf16x8, X[(wm * 64 + i * 16) * 8 + frag[q]]);
+                        for (int i = 0; i < NA; i++)
+                            xa[i] = __builtin_bit_cast(bf16x8, X[(rb0 + i * 16) * 8 + frag[q]]);
 #pragma unroll
                         for (int c = 0; c < 4; c++) wb[c] = __builtin_bit_cast(bf16x8, W[wcol(c) * 8 + frag[q]]);
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
+                        for (int i = 0; i < NA; i++)
 #pragma unroll
                             for (int c = 0; c < 4; c++)
                                 acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[c], xa[i], acc[i][c], 0, 0, 0);
@@ -211,10 +212,10 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                     const float ws0 = *(const __attribute__((address_space(4))) float*)(g.S0 + sidx + kb);
                     const float ws1 =
                         GATED ? *(const __attribute__((address_space(4))) float*)(g.S1 + sidx + kb) : ws0;
-                    i32x8 xa[4], wb[4];
+                    i32x8 xa[NA], wb[4];
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const i32x4 lo = X[(wm * 64 + i * 16) * 8 + frag[0]], hi = X[(wm * 64 + i * 16) * 8 + frag[1]];
+                    for (int i = 0; i < NA; i++) {
+                        const i32x4 lo = X[(rb0 + i * 16) * 8 + frag[0]], hi = X[(rb0 + i * 16) * 8 + frag[1]];
                         xa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     }
 #pragma unroll
@@ -224,8 +225,8 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                     }
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float sa = S[wm * 64 + i * 16 + r16];
+                    for (int i = 0; i < NA; i++) {
+                        const float sa = S[rb0 + i * 16 + r16];
 #pragma unroll
                         for (int c = 0; c < 4; c++) {
                             const f32x4 pr =
@@ -259,12 +260,11 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                 step(std::integral_constant<int, 2>{}, kb + 2);
             }
 
-            if (!active) return;
-            // lane (r16, kg) holds, for row block i and column block c, row wm*64 + 16 i + r16
+            // lane (r16, kg) holds, for row block i and column block c, row rb0 + 16 i + r16
             // and the 4 columns 16 c + 4 kg .. +3 of its column group
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int r = wm * 64 + i * 16 + r16;
+            for (int i = 0; i < NA; i++) {
+                const int r = rb0 + i * 16 + r16;
                 if (r >= rows) continue;
 #pragma unroll
                 for (int c = 0; c < (GATED ? 2 : 4); c++) {
