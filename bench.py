@@ -255,6 +255,51 @@ def traffic_from_profile(workload_name: str, stage: str):
         return None
 
 
+CALIBRATION_KERNEL = "CUDAFunctorOnSelf_add<float>"  # the 256 MiB copy of --calibrate
+HEADLINE_GATE_UP_KERNEL = "k_grouped_gemm_stream<true, false, 0,"  # bf16 gate/up, bf16 output
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, workload_name: str, stage: str = "gemm1") -> dict:
+    """HBM bytes per launch of the headline gate/up kernel from two rocprofv3 --pmc runs of
+    `bench.py --no-sweep --no-cpu --calibrate` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).
+    Each counter is scaled by what it reads for the calibration copy (256 MiB read, 256 MiB
+    written), so the result is in bytes whatever the counter's unit; the mean over the
+    kernel's dispatches is written to profiles/traffic.json with the kernel source hash."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        cal = [v for k, vs in vals.items() if CALIBRATION_KERNEL in k for v in vs]
+        ker = [(k, v) for k, vs in vals.items() if HEADLINE_GATE_UP_KERNEL in k for v in vs]
+        if not cal or not ker:
+            raise SystemExit(f"{path}: calibration or gate/up kernel dispatches not found")
+        factor = (256 << 20) / (sum(cal) / len(cal) * 1024)
+        out[key] = dict(kib=sum(v for _, v in ker) / len(ker), factor=factor, cal_kib=sum(cal) / len(cal),
+                        kernel=ker[0][0], launches=len(ker))
+    hbm = out["fetch"]["kib"] * 1024 * out["fetch"]["factor"] + out["write"]["kib"] * 1024 * out["write"]["factor"]
+    ent = dict(kernel=out["fetch"]["kernel"], fetch_kib_per_launch=round(out["fetch"]["kib"], 1),
+               write_kib_per_launch=round(out["write"]["kib"], 1),
+               calibration=dict(kernel=CALIBRATION_KERNEL, bytes_read=256 << 20, bytes_written=256 << 20,
+                                fetch_kib=round(out["fetch"]["cal_kib"], 1), write_kib=round(out["write"]["cal_kib"], 1),
+                                fetch_factor=round(out["fetch"]["factor"], 4),
+                                write_factor=round(out["write"]["factor"], 4)),
+               hbm_bytes_per_launch=int(hbm), launches=out["fetch"]["launches"], kernel_sha=kernel_hash())
+    rec = {workload_name: {stage: ent}}
+    with open(os.path.join(PROFILE_DIR, "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return ent
+
+
 def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
     """The CPU oracle (as it stands) on a bounded token sample of batch 0 of the workload."""
     import numpy as np
@@ -388,6 +433,9 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=12)
     ap.add_argument("--roofline-every", type=int, default=4,
                     help="time the dominant kernel with an event pair on every N-th timed step")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --no-sweep --no-cpu --calibrate` into profiles/traffic.json")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 256 MiB device copy (torch elementwise kernel): the reference launch "
                          "for scaling hardware byte counters")
@@ -401,6 +449,10 @@ def main():
         print(f"bench.py measures one GPU: this layer runs on a single MI355X (no collectives); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        ent = traffic_from_counters(*args.traffic_from, "bf16 H2048 I768 E128 top8, T=256, uniform")
+        print(json.dumps(ent))
+        return
 
     import torch
 
