@@ -101,6 +101,19 @@ def test_bf16_layer_2048x768_e128_top8_concentrated(T):
     check_layer(L, n_sample=24)
 
 
+@pytest.mark.parametrize("T", [128, 256])
+def test_fp8_layer_2048x768_e128_top8_concentrated(T):
+    # hot experts of ~120 / ~240 rows cut into 4 / 8 light tiles, no heavy launch
+    announce(f"fp8 H=2048 I=768 E=128 k=8 concentrated T={T}")
+    L = Layer(config=synth.FP8_LAYER, weight_config=synth.BF16_LAYER, T=T, H=2048, I=768, E=128, k=8, fp8=True,
+              routing="concentrated")
+    check_layer(L, n_sample=24)
+    ws = fm.workspace(L.shape)
+    L.forward(ws)
+    st = fm.fmoe_read_stats(ws)
+    assert st["heavy_tiles"] == 0 and st["max_rows"] > 2 * st["tile_rows"]
+
+
 @pytest.mark.parametrize("T", [64, 128, 256])
 def test_fp8_layer_2048x768_e128_top8(T):
     announce(f"fp8 H=2048 I=768 E=128 k=8 T={T}")
