@@ -40,6 +40,35 @@ __device__ __forceinline__ float key_float(uint32_t kb) {
     return __uint_as_float((kb & 0x80000000u) ? (kb & 0x7fffffffu) : ~kb);
 }
 
+// One step of the key max: each lane takes the larger of its key and the key the DPP control
+// CTRL brings it from another lane (lanes whose source is outside the row, or whose row is not
+// in ROWS, keep their own).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long key_max_step(unsigned long long v) {
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t nlo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+    const uint32_t nhi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+    const unsigned long long n = ((unsigned long long)nhi << 32) | nlo;
+    return n > v ? n : v;
+}
+
+// Largest 64-bit key of the wavefront, in every lane.  Row shifts by 1, 2, 4 and 8 leave each
+// 16-lane row's maximum in its lane 15 (a max-scan: taking a key twice does not matter), the
+// row broadcasts of lanes 15 and 31 carry it into the later rows, and lane 63 ends with the
+// maximum of all 64 lanes, which is then read as a uniform value.  Everything runs on the
+// vector ALU; a shuffle through the LDS crossbar per step would cost a round trip each.
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long v) {
+    v = key_max_step<0x111, 0xf>(v);  // row_shr:1
+    v = key_max_step<0x112, 0xf>(v);  // row_shr:2
+    v = key_max_step<0x114, 0xf>(v);  // row_shr:4
+    v = key_max_step<0x118, 0xf>(v);  // row_shr:8
+    v = key_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = key_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
 // Token t by the calling wavefront: ids [*,k] and weights [*,k] of row t; also the ids into
 // ids_lds[0..k) when ids_lds is not null.
 template <int SLOTS, bool BF16_IN>
@@ -73,12 +102,12 @@ __device__ __forceinline__ void topk_row(const void* __restrict__ logits, int t,
             unsigned long long b = 0ull;
 #pragma unroll
             for (int s = 0; s < SLOTS; s++) b = (grp[s] == g && key[s] > b) ? key[s] : b;
-            b = wave_max(b);
+            b = wave_max_key(b);
             if (lane == g) gk = b;
         }
         unsigned long long kept = 0ull;  // bit g: group g kept
         for (int j = 0; j < topk_group; j++) {
-            const unsigned long long b = wave_max(gk);  // group keys are distinct (distinct experts)
+            const unsigned long long b = wave_max_key(gk);  // group keys are distinct (distinct experts)
             const int g = __ffsll((long long)__ballot(gk == b && b != 0ull)) - 1;
             kept |= 1ull << g;
             if (lane == g) gk = 0ull;
@@ -94,7 +123,7 @@ __device__ __forceinline__ void topk_row(const void* __restrict__ logits, int t,
         unsigned long long best = key[0];
 #pragma unroll
         for (int s = 1; s < SLOTS; s++) best = key[s] > best ? key[s] : best;
-        best = wave_max(best);
+        best = wave_max_key(best);
         const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
         const float val = key_float((uint32_t)(best >> 32));
         if (lane == j) { my_v = val; my_id = e; }
