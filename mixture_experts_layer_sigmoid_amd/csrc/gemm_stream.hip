@@ -411,8 +411,9 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
 
 // Chunk length CS and weight ring depth D: bf16 8 and 8, FP8 4 and 4.  An FP8 down GEMM on
 // 32-row tiles whose reduction is a multiple of 6 steps (768 deep: 6 steps) takes chunks of 6
-// with a ring of 3 instead, so no chunk is padded past the reduction end (a third of the
-// steps with chunks of 4); measured 10% faster there.
+// instead, so no chunk is padded past the reduction end (a third of the steps with chunks of
+// 4; measured 10% faster there), with a ring of 2 (measured ~1 us faster than a ring of 3
+// and 4-6 us faster than a ring of 6 at 64-256 tokens of the 128-expert layer).
 template <bool GATED, bool FP8, int OUT>
 hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, int cus, hipStream_t st) {
     constexpr int CS = SCfg<FP8>::CS, D = FP8 ? 4 : 8;
@@ -420,7 +421,7 @@ hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, i
     if (tile_rows == 32) {
         if constexpr (FP8 && !GATED) {
             const int nsteps = a.K / SCfg<FP8>::KSTEP;
-            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT, 2, 6, 3>(a, max_tiles, cus, st);
+            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT, 2, 6, 2>(a, max_tiles, cus, st);
         }
         return launch_stream<GATED, FP8, OUT, 2, CS, D>(a, max_tiles, cus, st);
     }
