@@ -332,6 +332,57 @@ def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
                        f"OpenMP over tokens, {threads} threads on {platform.processor() or platform.machine()}")
 
 
+def cpu_oracle_sample(wl: Workload, cache: dict) -> dict:
+    """The CPU oracle (as it stands) on one token sample of a sweep workload's batch 0: the first
+    max(threads, 8) tokens (all of them below that), the router on all T tokens.  Only the local
+    experts those tokens pick are generated, from the same per-expert streams as the GPU's
+    weights (FP8: quantised with the same offline routine), and handed to the oracle as a compact
+    expert set; generated experts are kept in `cache` for the next workloads.  The expert time is
+    extrapolated to the call by OpenMP rounds of `threads` tokens."""
+    import numpy as np
+
+    import oracle
+    from mixture_experts_layer_sigmoid_amd import synth
+
+    x = synth.activations(wl.config, wl.T, wl.H, seed=0)
+    lg = synth.routed_logits(wl.config, wl.T, wl.E, wl.k, wl.routing, seed=0)
+    t0 = time.perf_counter()
+    ids, w = oracle.router_topk(synth.bf16_bits(lg), wl.k)
+    route_s = time.perf_counter() - t0
+    threads = oracle.num_threads()
+    n = min(wl.T, max(threads, 8))
+    lo = wl.ep_rank * wl.El
+    local = sorted({int(e) for e in ids[:n].ravel() if lo <= e < lo + wl.El})
+
+    def expert(gid):
+        key = (wl.weight_config, wl.H, wl.I, gid, wl.fp8)
+        if key not in cache:
+            ws = synth.expert_weights_bf16(wl.weight_config, 1, wl.H, wl.I, gid)
+            if wl.fp8:
+                q = [synth.block_quantize_fp8(t) for t in ws]
+                cache[key] = tuple(c.numpy() for c, _ in q) + tuple(s.numpy() for _, s in q)
+            else:
+                cache[key] = tuple(synth.bf16_bits(t) for t in ws)
+        return cache[key]
+
+    parts = [expert(g) for g in local]
+    spent = 0.0
+    if parts:
+        cat = [np.ascontiguousarray(np.concatenate([p[i] for p in parts])) for i in range(len(parts[0]))]
+        ids_c = np.full(ids.shape, -1, np.int32)
+        for i, g in enumerate(local):
+            ids_c[ids == g] = i
+        sc = dict(sg=cat[3], su=cat[4], sd=cat[5]) if wl.fp8 else {}
+        t0 = time.perf_counter()
+        oracle.moe_tokens(synth.bf16_bits(x), ids_c, w, cat[0], cat[1], cat[2], E=len(local),
+                          tokens=np.arange(n, dtype=np.int32), **sc)
+        spent = time.perf_counter() - t0
+    per_call = spent / math.ceil(n / threads) * math.ceil(wl.T / threads) + route_s
+    return dict(cpu_oracle_us=round(per_call * 1e6, 1),
+                cpu_sample=f"{n} of {wl.T} tokens of batch 0 ({len(local)} local experts, {spent:.2f} s), router on "
+                           f"all tokens, {threads} threads")
+
+
 def tile_sweep(workloads, steps: int = 10) -> list:
     """Tile-space sweep: every tile plan the library can run (light tile rows 16/32 x gate/up
     reduction split 1/2/4 x down split 1/2/4 x light tiles per expert 1/8) against the host
@@ -514,6 +565,16 @@ def main():
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(head)
+        hs.update(cpu_oracle_us=cpu["us_per_call"], cpu_sample=cpu["sample"])
+        if not args.no_sweep:
+            cache = {}
+            for wl, rec in zip(sweep_workloads(B3, synth), sweep[1:]):
+                print(f"[bench] cpu oracle sample: {wl.name}", file=sys.stderr, flush=True)
+                try:
+                    rec.update(cpu_oracle_sample(wl, cache))
+                except Exception as e:  # the GPU figures stand without it
+                    rec.update(cpu_oracle_us=None, cpu_sample=f"failed: {e!r}")
+            del cache
 
     line = dict(metric=METRIC, value=round(value, 4), unit="TB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                 ms_per_step=round(m["wall_s"] * 1e3, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
