@@ -89,11 +89,12 @@ typedef struct {
     int32_t empty_experts;   /* local experts with no row                                   */
     int32_t m_tiles;         /* row tiles of the grouped GEMMs (light + heavy)              */
     int32_t rows_estimate;   /* host plan: max(1, ceil(T*top_k/E))                          */
-    int32_t tile_rows;       /* host plan: largest light tile (one per expert with 1..tile_rows
-                                rows); heavier experts are cut into heavy tiles              */
-    int32_t heavy_tiles;     /* row tiles of experts with more than tile_rows rows           */
+    int32_t tile_rows;       /* host plan: largest light tile; an expert with 1..tile_rows rows
+                                is one light tile, a heavier one heavy tiles (FP8 when every
+                                expert fits 8 light tiles: ceil(c / tile_rows) light tiles)  */
+    int32_t heavy_tiles;     /* row tiles of the experts cut into heavy tiles               */
     int32_t heavy_rows;      /* host plan: rows of a full heavy tile (an expert with c rows
-                                gets c / heavy_rows full tiles and one with the rest)        */
+                                gets ceil(c / heavy_rows) tiles of about equal size)         */
 } fmoe_stats;
 
 int fmoe_abi_version(void);
