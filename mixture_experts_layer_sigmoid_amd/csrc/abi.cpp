@@ -334,7 +334,7 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
         const Layout& L = p.L;
         MTile* mtiles = (MTile*)(wsb + L.mtiles);
         FMOE_TRY(launch_route_group(logits, bf16, (int)p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, p.El, p.lo,
-                                    p.tile_rows, p.heavy_rows, p.rows_estimate, (int32_t*)(wsb + L.counts),
+                                    p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate, (int32_t*)(wsb + L.counts),
                                     (int32_t*)(wsb + L.offsets), (int32_t*)(wsb + L.perm), (int32_t*)(wsb + L.inv),
                                     mtiles, mtiles + p.max_light, (DevHeader*)(wsb + L.hdr), st, xqp));
         return run_experts(p, x, ids, wts, w, out, wsb, st, ev, true, p.fp8);

@@ -40,8 +40,8 @@ size_t group_scratch_bytes(long long n, int El);
 // Router top-k (plain) and grouping in one launch, for small T: route_group_fits says when.
 bool route_group_fits(int T, int k, int E, int El);
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
-                              int32_t* ids, float* weights, int El, int lo, int tile_rows, int heavy_rows,
-                              int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
+                              int heavy_rows, int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                               int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st,
                               const XQuant* xq = nullptr);
 // light_cap >= tile_rows: experts with up to light_cap rows are cut into light tiles of tile_rows

@@ -269,9 +269,9 @@ def test_every_tile_plan_matches_the_oracle(fp8):
 
 # Up to 16 tokens the forward routes and groups in one launch (wavefront t routes token t and
 # the same workgroup then groups the ids from LDS: one wavefront for up to 64 assignments, the
-# whole workgroup above).  Its routing must equal the router
-# kernel's bit for bit, its grouping the grouping kernel's (same stats, identical output of
-# fmoe_experts on the same ids), and the output the oracle's; T = 17 takes the two-launch path.
+# whole workgroup above).  Its routing must equal the router kernel's bit for bit, its grouping
+# the grouping kernel's (same stats, identical output of fmoe_experts on the same ids), and the
+# output the oracle's; from T = 17 on the forward takes the two-launch path, held to the same.
 @pytest.mark.parametrize("T,H,I,E,k,ep,fp8,scoring,fp32", [
     (1, 256, 128, 128, 8, 1, False, "softmax", False),
     (3, 256, 256, 400, 6, 8, True, "sigmoid", False),    # E > 256: 8 slots per lane; rank 7 of 8
@@ -279,6 +279,9 @@ def test_every_tile_plan_matches_the_oracle(fp8):
     (16, 256, 128, 1000, 64, 2, False, "softmax", False),  # 16 slots, k = 64: 16 chunks of 64
     (4, 256, 128, 1000, 16, 2, False, "sigmoid", False),   # 64 assignments, one wavefront groups; rank 1 of 2
     (17, 256, 128, 64, 8, 1, False, "softmax", False),   # one past the fused limit
+    (32, 256, 128, 64, 8, 1, False, "softmax", False),   # 256 assignments, 32-row light tiles
+    (64, 256, 128, 16, 4, 1, False, "sigmoid", True),    # heavy launch possible
+    (40, 256, 256, 32, 2, 1, True, "softmax", False),    # FP8: several light tiles per expert allowed
 ])
 def test_small_batch_fused_router_and_grouping(T, H, I, E, k, ep, fp8, scoring, fp32):
     announce(f"fused router+grouping T={T} H={H} I={I} E={E} k={k} ep={ep} fp8={fp8} {scoring} fp32={fp32}")
