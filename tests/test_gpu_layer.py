@@ -166,6 +166,25 @@ def test_fp8_forward_quantises_x_in_the_router_launch(T):
     check_layer(L, n_sample=10 ** 6)
 
 
+# The gate/up kernel that quantises h in its epilogue (light tiles only) against the separate
+# quantisation kernel (used whenever heavy tiles may exist): on a batch whose experts all fit a
+# light tile, both plans cut the same tiles, so the outputs must agree bit for bit.
+@pytest.mark.parametrize("T,H,I,E,k", [(40, 256, 384, 16, 1), (60, 512, 256, 8, 2)])
+def test_fp8_fused_h_quantisation_equals_the_quantisation_kernel(T, H, I, E, k):
+    announce(f"fp8 fused h quantisation vs quantisation kernel T={T} H={H} I={I} E={E} k={k}")
+    L = Layer(config=99, T=T, H=H, I=I, E=E, k=k, fp8=True)
+    ws = fm.workspace(L.shape)
+    L.plan = fm.fmoe_plan(32, 1, 1, 8)  # every expert light: gate/up writes e4m3 codes itself
+    fused = L.forward(ws)[0]
+    st = fm.fmoe_read_stats(ws)
+    assert st["heavy_tiles"] == 0 and st["max_rows"] <= 32
+    L.plan = fm.fmoe_plan(32, 1, 1, 1)  # heavy launch possible (T > 32): fp32 h, then the kernel
+    separate = L.forward(ws)[0]
+    assert fm.fmoe_read_stats(ws)["heavy_tiles"] == 0
+    assert torch.equal(fused, separate)
+    check_layer(L, n_sample=10 ** 6)
+
+
 @pytest.mark.parametrize("T", [12, 40])
 def test_fp8_nan_activation_rows_stay_in_their_tokens(T):
     announce(f"fp8 layer with NaN rows of x, T={T}")
