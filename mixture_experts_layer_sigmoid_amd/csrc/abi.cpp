@@ -105,13 +105,17 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr, long long max
     // below 16 expected rows per expert (T=8: 133 -> 118 us, T=32: 225 -> 212 us) and from 32
     // on, where the light tiles are the few experts left below 17 rows (T=512: equal under
     // uniform routing, 311 -> 289 us under concentrated routing), and the down GEMM at one
-    // expected row (T=8: 118 -> 111 us); FP8 tiles stream best unsplit there.
+    // expected row (T=8: 118 -> 111 us).  FP8 tiles stream best unsplit at a 2048-deep
+    // reduction (T=128: 141 against 150 us split), but a gate/up reduction of 4096 or more
+    // splits better in two (the 7168-wide expert shard at T=288: 433 against 440 us uniform,
+    // 325 against 331 us concentrated).
     const long long local_rows = (p.n * p.El + p.E - 1) / p.E;
     const long long active = local_rows < p.El ? local_rows : p.El;
     auto pick_wk = [&](int N, bool gate_up) {
         const long long tasks = active * (N / 16);
         if (tasks < 1024) return 4;
         if (!p.fp8 && (gate_up ? p.rows_estimate < 16 || p.rows_estimate >= 32 : p.rows_estimate <= 1)) return 2;
+        if (p.fp8 && gate_up && p.H >= 4096) return 2;
         return tasks < 2048 ? 2 : 1;
     };
     p.wk1 = ov && ov->split_gate_up ? ov->split_gate_up : pick_wk(p.I, true);
