@@ -118,6 +118,10 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr, long long max
         // four wavefronts per stream were as fast under uniform routing and faster under
         // concentrated routing (T=8: 107.6 / 47.9 us against 107.0 / 50.7 us split in two)
         if (!p.fp8 && gate_up && p.rows_estimate <= 1) return 4;
+        // from 128 expected rows on the light tiles are the few experts left below 17 rows, each
+        // a short stream: splits of 4 (gate/up) and 2 (down) measured best under uniform and
+        // concentrated routing (T=4096: 537 / 603 us against 540 / 620 us with 2 and 1)
+        if (!p.fp8 && p.rows_estimate >= 128) return gate_up ? 4 : 2;
         if (!p.fp8 && (gate_up ? p.rows_estimate < 16 || p.rows_estimate >= 32 : p.rows_estimate <= 1)) return 2;
         if (p.fp8 && gate_up && p.H >= 4096) return 2;
         return tasks < 2048 ? 2 : 1;
