@@ -38,14 +38,13 @@ constexpr int kScanShared = 96 + 64 + 1536;  // LDS ints of scan_and_tile (kScan
 // local expert (-1 when not local) and its rank inside the chunk; *bad gets the number of
 // ids outside [0, E) in the chunk (same value in every lane).  `mask` is per-wavefront LDS
 // scratch of El entries.
-__device__ void chunk_rank(const int32_t* __restrict__ ids, int n, int E, int El, int lo, int chunk, int* col,
-                           int col_stride, int* mask, int* out_l, int* out_r, int* bad) {
+// chunk_rank_id takes this lane's id already loaded (valid: the lane holds an assignment).
+__device__ void chunk_rank_id(int id, bool valid, int E, int El, int lo, int* col, int col_stride, int* mask,
+                              int* out_l, int* out_r, int* bad) {
     const int lane = lane_id();
     for (int e = lane; e < El; e += 64) mask[e] = 0;
-    const int i = chunk * 64 + lane;
     int l = -1, b = 0;
-    if (i < n) {
-        const int id = ids[i];
+    if (valid) {
         if (id < 0 || id >= E) b = 1;
         else if (id - lo >= 0 && id - lo < El) l = id - lo;
     }
@@ -71,6 +70,12 @@ __device__ void chunk_rank(const int32_t* __restrict__ ids, int n, int E, int El
     for (int e = lane; e < El; e += 64) col[e * col_stride] = mask[e];
     *out_l = l;
     *out_r = r;
+}
+
+__device__ __forceinline__ void chunk_rank(const int32_t* __restrict__ ids, int n, int E, int El, int lo, int chunk,
+                                           int* col, int col_stride, int* mask, int* out_l, int* out_r, int* bad) {
+    const int i = chunk * 64 + lane_id();
+    chunk_rank_id(i < n ? ids[i] : 0, i < n, E, El, lo, col, col_stride, mask, out_l, out_r, bad);
 }
 
 // Exclusive sums of four values over the kScanThreads threads of the workgroup (thread
@@ -291,7 +296,14 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
     int* bads = mask + NW * El;            // [kSmallChunks]
     int* sh = bads + kSmallChunks;         // scan scratch [kScanShared]
     const int w = threadIdx.x >> 6;
-    // wavefront w ranks chunks w, w + NW, ...
+    // wavefront w ranks chunks w, w + NW, ...; the ids of all its chunks are loaded first, so
+    // the wavefront waits for memory once rather than once per chunk
+    int idv[kSmallPerWave];
+#pragma unroll
+    for (int j = 0; j < kSmallPerWave; j++) {
+        const int i = (w + j * NW) * 64 + lane_id();
+        idv[j] = i < n ? ids[i] : 0;
+    }
     int l[kSmallPerWave], r[kSmallPerWave];
 #pragma unroll
     for (int j = 0; j < kSmallPerWave; j++) {
@@ -299,7 +311,8 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
         l[j] = r[j] = -1;
         if (c < nchunk) {
             int bad = 0;
-            chunk_rank(ids, n, E, El, lo, c, cnt + c * El, 1, mask + w * El, &l[j], &r[j], &bad);
+            chunk_rank_id(idv[j], c * 64 + lane_id() < n, E, El, lo, cnt + c * El, 1, mask + w * El, &l[j], &r[j],
+                          &bad);
             if (lane_id() == 0) bads[c] = bad;
         }
     }
