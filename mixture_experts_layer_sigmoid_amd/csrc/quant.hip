@@ -9,6 +9,8 @@
 // IMA" (Root cause) calls a NaN firewall.  IEEE division (no fast-math), so codes and scales
 // are reproducible bit for bit.  The forward quantises x in the router launch instead, with the
 // same per-group code.
+#include <climits>
+
 #include "launch.hpp"
 
 namespace fmoe {
@@ -24,7 +26,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
     const int lane = lane_id();
     const int G = cols >> 7;
     const long long row = g / G;
-    if (rows_hdr && row >= rows_hdr->local_rows) return;
+    // the row count and the values are loaded together: rows past the count still lie inside
+    // the buffer (sized for every assignment), and nothing is stored for them
+    const int live_rows = rows_hdr ? rows_hdr->local_rows : INT_MAX;
     const int grp = (int)(g - row * G);
     const size_t base = (size_t)row * cols + (size_t)grp * 128 + lane * 2;
     float a, b;
@@ -37,6 +41,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const void* __restrict__ x, 
         a = two.x;
         b = two.y;
     }
+    if (row >= live_rows) return;  // the whole wavefront: one row per wavefront
     quant_group_wave(a, b, q + base, s + g);
 }
 
