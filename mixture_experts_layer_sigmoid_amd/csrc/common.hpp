@@ -36,7 +36,8 @@ static_assert(sizeof(DevHeader) == 64, "header size");
 
 // One row tile of a grouped GEMM: local expert, first grouped row, number of rows.
 // Heavy tiles also carry, in `group`, their index among the heavy tiles of their expert (low
-// 16 bits) and that expert's heavy tile count (high 16 bits); light tiles carry 0.
+// 16 bits) and that expert's heavy tile count (high 16 bits, read as unsigned: it reaches
+// 32768); light tiles carry 0.
 struct MTile {
     int32_t expert, row0, rows, group;
 };

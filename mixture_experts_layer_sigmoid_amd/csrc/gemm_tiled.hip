@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
         // here: scalar loads through the constant address space.
         const int i0 = t / nblocks;
         const i32x4 m0 = *(const __attribute__((address_space(4))) i32x4*)(g.mtiles + i0);
-        const int m = m0[3] >> 16, first = i0 - (m0[3] & 0xffff);
+        // unsigned: an expert's tile count reaches 32768 (2^23 rows of 256), bit 31 of the field
+        const int m = (int)((uint32_t)m0[3] >> 16), first = i0 - (m0[3] & 0xffff);
         const int tl = t - first * nblocks;
         const int nb = tl / m;
         const int tile = first + (tl - nb * m);

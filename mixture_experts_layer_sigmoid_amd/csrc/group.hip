@@ -248,7 +248,8 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
                 mt.expert = e;
                 mt.row0 = my_first + j * hrows;
                 mt.rows = min(hrows, total - j * hrows);
-                mt.group = j | (nheavy << 16);  // nheavy <= 2^23 / 256
+                // nheavy <= 2^23 / 256 = 32768 (bit 31 when it is 32768: read back unsigned)
+                mt.group = (int)((uint32_t)j | ((uint32_t)nheavy << 16));
                 mtiles_heavy[my_hfirst + j] = mt;
             }
         }

@@ -250,6 +250,25 @@ def test_random_small_shapes_match_the_oracle(case):
     check_layer(L, n_sample=10 ** 6)
 
 
+# The library's declared size limits and large batches: hidden or inter at 65536 (bf16 and FP8;
+# FP8 32-row split tiles would overflow 64 KB of scales, so the plan takes 16-row tiles), 1024
+# local experts with top-64 routing, one expert holding 65536 rows (256 heavy tiles), and 2^20
+# assignments (16384 grouping chunks); sampled tokens against the oracle.
+@pytest.mark.parametrize("T,H,I,E,k,fp8,n_sample", [
+    (3, 65536, 128, 2, 2, False, 10 ** 6),
+    (3, 65536, 128, 2, 1, True, 10 ** 6),
+    (2, 128, 65536, 2, 1, False, 10 ** 6),
+    (2, 128, 65536, 2, 2, True, 10 ** 6),
+    (32, 128, 128, 1024, 64, False, 10 ** 6),
+    (65536, 128, 128, 1, 1, False, 48),
+    (131072, 128, 128, 16, 8, False, 48),
+])
+def test_size_limits_and_large_batches(T, H, I, E, k, fp8, n_sample):
+    announce(f"size limits T={T} H={H} I={I} E={E} k={k} fp8={fp8}")
+    L = Layer(config=97, T=T, H=H, I=I, E=E, k=k, fp8=fp8)
+    check_layer(L, n_sample=n_sample)
+
+
 def test_forward_is_deterministic_and_matches_experts():
     announce("determinism and forward == router + experts")
     L = Layer(config=synth.BF16_LAYER, T=256, H=2048, I=768, E=128, k=8, routing="concentrated")
