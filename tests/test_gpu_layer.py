@@ -269,6 +269,28 @@ def test_size_limits_and_large_batches(T, H, I, E, k, fp8, n_sample):
     check_layer(L, n_sample=n_sample)
 
 
+def test_all_assignments_on_one_expert_at_the_assignment_limit():
+    # caller ids may repeat: 2^20 tokens x top-8, every id 0, is 2^23 rows (the limit) on one
+    # expert, cut into 32768 heavy tiles (the count fills the top 16 bits of the tile field)
+    T, H, I, E, k = 1 << 20, 128, 128, 8, 8
+    announce(f"fmoe_experts: {T * k} rows on one expert")
+    L = synth.tiny_layer(4, H, E, I, seed=7)  # weights only
+    x = synth.activations(98, T, H)
+    ids = np.zeros((T, k), np.int32)
+    wts = np.random.default_rng(3).random((T, k)).astype(np.float32)
+    shape = fm.make_shape(T, H, I, E, k)
+    ws = fm.workspace(shape)
+    w = fm.ExpertWeights(L["wg"].cuda(), L["wu"].cuda(), L["wd"].cuda())
+    out = fm.fmoe_experts(shape, x.cuda(), torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda(), w, ws=ws)
+    st = fm.fmoe_read_stats(ws)
+    assert st["local_rows"] == T * k and st["max_rows"] == T * k and st["heavy_tiles"] == T * k // 256
+    tok = sample_tokens(T, 48)
+    ref = oracle.moe_tokens(synth.bf16_bits(x), ids, wts.astype(np.float64),
+                            *(synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")), E=E, tokens=tok)
+    assert row_rel_err(out.float().cpu().numpy()[tok], ref) <= BF16_TOL
+    del ws, out
+
+
 def test_forward_is_deterministic_and_matches_experts():
     announce("determinism and forward == router + experts")
     L = Layer(config=synth.BF16_LAYER, T=256, H=2048, I=768, E=128, k=8, routing="concentrated")
