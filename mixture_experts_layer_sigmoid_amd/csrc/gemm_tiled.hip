@@ -14,8 +14,9 @@
 // four SIMDs equally, carry MFMA work whatever the tile's size.
 // Every 128-byte slice of the reduction (64 bf16 or 128 e4m3 per row) is one stage: the
 // activation rows (gathered through the row map) and the weight rows are copied straight from
-// global memory into LDS by direct global-to-LDS loads, three stages deep, so two stages are in
-// flight while one is read.  A stage row of 8 pieces of 16 bytes keeps piece c at position
+// global memory into LDS by direct global-to-LDS loads: the activations three stages deep, the
+// weights four stages deep for bf16 (160 KB in all) and three for FP8, so two activation and
+// three (FP8: two) weight stages are in flight while one is read.  A stage row of 8 pieces of 16 bytes keeps piece c at position
 // c ^ ((row >> 1) & 7): the 16 rows read by one MFMA fragment then fall in 16 different bank
 // groups.  Each buffer is a separate LDS array and every wait is an explicit count of the loads
 // that must have landed, so the compiler never has to wait for loads into another buffer.
@@ -66,6 +67,14 @@ __device__ __forceinline__ void tg_static_for(F&& f) {
     }
 }
 
+// f(0), f(1), .. while f returns true, each call nested in the previous one's success branch
+template <int I, int N, typename F>
+__device__ __forceinline__ void tg_static_chain(F&& f) {
+    if constexpr (I < N) {
+        if (f(std::integral_constant<int, I>{})) tg_static_chain<I + 1, N>(f);
+    }
+}
+
 __device__ __forceinline__ float tg_silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // position of piece c of stage row r
@@ -73,8 +82,11 @@ __device__ __forceinline__ int tg_slot(int r, int c) { return r * 8 + (c ^ ((r >
 
 template <bool GATED, bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
+    // bf16: three activation and four weight buffers, 3 x 32 KB + 4 x 16 KB = 160 KB of LDS;
+    // FP8 keeps three weight buffers (its activation scales take the room of the fourth)
+    constexpr int NW = FP8 ? 3 : 4;
     __shared__ i32x4 X0[kTgXPieces], X1[kTgXPieces], X2[kTgXPieces];
-    __shared__ i32x4 W0[kTgWPieces], W1[kTgWPieces], W2[kTgWPieces];
+    __shared__ i32x4 W0[kTgWPieces], W1[kTgWPieces], W2[kTgWPieces], W3[NW > 3 ? kTgWPieces : 1];
     __shared__ float SA0[FP8 ? kTgRows : 1], SA1[FP8 ? kTgRows : 1], SA2[FP8 ? kTgRows : 1];
 
     const int lane = lane_id();
@@ -120,7 +132,8 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
 
         auto run = [&](auto NAc) {
             constexpr int NA = decltype(NAc)::value;  // activation loads per stage = 64-row groups
-            constexpr int L = NA + 2 + (FP8 ? 1 : 0);  // vector-memory instructions per stage
+            constexpr int LX = NA + (FP8 ? 1 : 0);  // vector-memory instructions per activation stage
+            constexpr int LW = 2;                   // and per weight stage
             // activation pieces: load j of wavefront w covers stage rows (j*8 + w)*8 .. +8
             size_t xoff[NA];
 #pragma unroll
@@ -156,24 +169,30 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                 ssrc = (g.perm_src ? g.perm_src[p] : p) / topk;
             }
 
-            auto issue = [&](auto Bc, int kb) {
+            // activation stage kb into buffer X<B> (FP8: with its activation scales)
+            auto issue_x = [&](auto Bc, int kb) {
                 constexpr int B = decltype(Bc)::value;
                 i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
-                i32x4* W = B == 0 ? W0 : B == 1 ? W1 : W2;
                 const size_t ko = (size_t)kb * 128;
 #pragma unroll
                 for (int j = 0; j < NA; j++)
                     __builtin_amdgcn_global_load_lds((gbl_void*)((const uint8_t*)g.A + xoff[j] + ko),
                                                      (lds_void*)(X + (j * 8 + w) * 64), 16, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    __builtin_amdgcn_global_load_lds((gbl_void*)(wsrc[j] + ko), (lds_void*)(W + (j * 8 + w) * 64), 16,
-                                                     0, 0);
                 if constexpr (FP8) {
                     float* S = B == 0 ? SA0 : B == 1 ? SA1 : SA2;
                     __builtin_amdgcn_global_load_lds((gbl_void*)(g.A_scale + (size_t)ssrc * nkb128 + kb),
                                                      (lds_void*)(S + (w & 3) * 64), 4, 0, 0);
                 }
+            };
+            // weight stage kb into buffer W<B>
+            auto issue_w = [&](auto Bc, int kb) {
+                constexpr int B = decltype(Bc)::value;
+                i32x4* W = B == 0 ? W0 : B == 1 ? W1 : B == 2 ? W2 : W3;
+                const size_t ko = (size_t)kb * 128;
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    __builtin_amdgcn_global_load_lds((gbl_void*)(wsrc[j] + ko), (lds_void*)(W + (j * 8 + w) * 64), 16,
+                                                     0, 0);
             };
 
             f32x4 acc[NA][4];
@@ -189,10 +208,10 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
             const int fb = GATED ? nb / 2 : nb;
             const size_t sidx = ((size_t)expert * (g.N / 128) + fb) * nkb128;
 
-            auto compute = [&](auto Bc, int kb) {
-                constexpr int B = decltype(Bc)::value;
+            auto compute = [&](auto BXc, auto BWc, int kb) {
+                constexpr int B = decltype(BXc)::value, BW = decltype(BWc)::value;
                 const i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
-                const i32x4* W = B == 0 ? W0 : B == 1 ? W1 : W2;
+                const i32x4* W = BW == 0 ? W0 : BW == 1 ? W1 : BW == 2 ? W2 : W3;
                 if constexpr (!FP8) {
 #pragma unroll
                     for (int q = 0; q < 2; q++) {
@@ -240,26 +259,49 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                 }
             };
 
-            // stage kb from buffer B: wait for it (this wavefront's loads, then everyone's),
-            // which also means every wavefront is done with stage kb-1, whose buffer then takes
-            // stage kb+2.  Every step issues its loads and waits for the same count, so the
-            // compiler's own count of the loads in flight is the same on every path: steps
-            // past the end reload the last stage (from L2) and compute nothing.
-            auto step = [&](auto Bc, int kb) {
-                constexpr int B = decltype(Bc)::value;
-                tg_wait_vmcnt<L>();
+            // Stage s sits in X<s % 3> and W<s % NW>.  The step of stage s waits for it (this
+            // wavefront's loads, then everyone's), which also means every wavefront is done with
+            // stage s-1, whose buffers then take activation stage s+2 and weight stage s+NW-1:
+            // with four weight buffers the weights run one stage further ahead than the
+            // activations.  Loads land in issue order, so the wait is a count of the loads issued
+            // after the last one of stage s: NW = 3 (issue order X2 W2 X3 W3 ..): the next step's
+            // X and W; NW = 4 (W0 X0 W1 X1 W2, then X2 W3 X3 W4 ..): a W, then the next X and W.
+            // The last steps reload the last stage (from L2) in place of the stages past the end.
+            constexpr int WAIT = NW == 3 ? LX + LW : LX + 2 * LW;
+            auto step = [&](auto Jc, int kb) {
+                constexpr int J = decltype(Jc)::value;
+                tg_wait_vmcnt<WAIT>();
                 tg_barrier();
-                issue(std::integral_constant<int, (B + 2) % 3>{}, min(kb + 2, nkb - 1));
-                if (kb < nkb) compute(Bc, kb);
+                issue_x(std::integral_constant<int, (J + 2) % 3>{}, min(kb + 2, nkb - 1));
+                issue_w(std::integral_constant<int, (J + NW - 1) % NW>{}, min(kb + NW - 1, nkb - 1));
+                compute(std::integral_constant<int, J % 3>{}, std::integral_constant<int, J % NW>{}, kb);
             };
 
-            issue(std::integral_constant<int, 0>{}, 0);
-            issue(std::integral_constant<int, 1>{}, min(1, nkb - 1));
-            for (int kb = 0; kb < nkb; kb += 3) {
-                step(std::integral_constant<int, 0>{}, kb);
-                step(std::integral_constant<int, 1>{}, kb + 1);
-                step(std::integral_constant<int, 2>{}, kb + 2);
+            if constexpr (NW == 3) {
+                issue_x(std::integral_constant<int, 0>{}, 0);
+                issue_w(std::integral_constant<int, 0>{}, 0);
+                issue_x(std::integral_constant<int, 1>{}, min(1, nkb - 1));
+                issue_w(std::integral_constant<int, 1>{}, min(1, nkb - 1));
+            } else {
+                issue_w(std::integral_constant<int, 0>{}, 0);
+                issue_x(std::integral_constant<int, 0>{}, 0);
+                issue_w(std::integral_constant<int, 1>{}, min(1, nkb - 1));
+                issue_x(std::integral_constant<int, 1>{}, min(1, nkb - 1));
+                issue_w(std::integral_constant<int, 2>{}, min(2, nkb - 1));
             }
+            // Whole cycles of both buffer rings, unrolled so every buffer index is a constant,
+            // then the remaining steps as nested conditions: the path back to the loop head is
+            // always a whole cycle, and a skipped step skips all later ones, so the compiler's
+            // count of the loads in flight never merges two different paths before a step.
+            constexpr int U = NW == 3 ? 3 : 12;
+            int kb = 0;
+            for (; kb + U <= nkb; kb += U)
+                tg_static_for<0, U>([&](auto Jc) { step(Jc, kb + decltype(Jc)::value); });
+            tg_static_chain<0, U - 1>([&](auto Jc) {
+                if (kb + decltype(Jc)::value >= nkb) return false;
+                step(Jc, kb + decltype(Jc)::value);
+                return true;
+            });
 
             // lane (r16, kg) holds, for row block i and column block c, row rb0 + 16 i + r16
             // and the 4 columns 16 c + 4 kg .. +3 of its column group
@@ -291,13 +333,15 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
         else if (groups > 1) run(std::integral_constant<int, 2>{});
         else run(std::integral_constant<int, 1>{});
     }
+    // the last steps' loads into LDS land before the workgroup (and its LDS) goes away
+    tg_wait_vmcnt<0>();
 }
 
 template <bool GATED, bool FP8, bool OUT_F32>
 hipError_t launch_tiled(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
     const int per_task = GATED ? kTgCols / 2 : kTgCols;
     long long grid = (long long)max_tiles * (a.N / per_task);
-    if (grid > cus) grid = cus;  // one workgroup per CU (the three stages take 144 KB of LDS)
+    if (grid > cus) grid = cus;  // one workgroup per CU (the stage buffers take 144 to 160 KB of LDS)
     if (grid < 1) grid = 1;
     k_grouped_gemm_tiled<GATED, FP8, OUT_F32><<<(unsigned)grid, kTgThreads, 0, st>>>(a);
     return hipGetLastError();
