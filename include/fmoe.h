@@ -42,7 +42,7 @@ extern "C" {
 
 #define FMOE_ABI_VERSION 2
 
-/* Limits of this build (checked, FMOE_ERR_UNSUPPORTED beyond them). */
+/* Limits of the library (checked, FMOE_ERR_UNSUPPORTED beyond them). */
 #define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
 #define FMOE_MAX_TOP_K 64         /* top_k                                                     */
 #define FMOE_MAX_DIM 65536        /* hidden and inter                                          */
@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
     FMOE_OK = 0,
     FMOE_ERR_ARG = 1,          /* null pointer, misaligned pointer, inconsistent sizes   */
-    FMOE_ERR_UNSUPPORTED = 2,  /* a size or dtype outside the limits of this build       */
+    FMOE_ERR_UNSUPPORTED = 2,  /* a size or dtype outside the limits of the library      */
     FMOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than fmoe_workspace_bytes              */
     FMOE_ERR_HIP = 4           /* a HIP launch or runtime call failed                    */
 } fmoe_status;
