@@ -250,6 +250,21 @@ def test_random_small_shapes_match_the_oracle(case):
     check_layer(L, n_sample=10 ** 6)
 
 
+# Heavy row tiles at the shortest reductions and at stage counts that end inside a cycle of the
+# heavy kernel's buffer rings (bf16: 64-deep stages, 12 per cycle; FP8: 128-deep stages, 3 per
+# cycle): K = 128 gives 2 bf16 stages and a single FP8 stage.  About 300 rows per expert, so
+# experts are cut into one or two heavy tiles.
+@pytest.mark.parametrize("H,I", [(128, 128), (128, 384), (640, 256), (1152, 896)])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_heavy_tiles_at_short_and_ragged_reductions(H, I, fp8):
+    announce(f"heavy tiles H={H} I={I} fp8={fp8}")
+    L = Layer(config=96, T=600, H=H, I=I, E=4, k=2, fp8=fp8)
+    ws = fm.workspace(L.shape)
+    fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws)
+    assert fm.fmoe_read_stats(ws)["heavy_tiles"] >= 4
+    check_layer(L, n_sample=10 ** 6)
+
+
 # The library's declared size limits and large batches: hidden or inter at 65536 (bf16 and FP8;
 # FP8 32-row split tiles would overflow 64 KB of scales, so the plan takes 16-row tiles), 1024
 # local experts with top-64 routing, one expert holding 65536 rows (256 heavy tiles), and 2^20
