@@ -55,6 +55,9 @@ def _load():
         lib.oracle_act_quant.argtypes = [P, i, i, P, P]
         lib.oracle_moe_tokens.argtypes = [i] * 8 + [P] * 9 + [P, i, P]
         lib.oracle_num_threads.restype = i
+        lib.oracle_set_num_threads.argtypes = [i]
+        lib.oracle_grouped_gemm.restype = i
+        lib.oracle_grouped_gemm.argtypes = [i] * 9 + [P, P, P, i, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -190,6 +193,41 @@ def moe_tokens(x_bf16, ids, w, wg, wu, wd, *, E, ep_size=1, ep_rank=0, sg=None, 
     _load().oracle_moe_tokens(T, H, I, E, k, ep_size, ep_rank, int(fp8), _p(x), _p(ids), _p(w),
                               _p(wg), _p(wu), _p(wd), _p(sg), _p(su), _p(sd), _p(tok), len(tok), _p(out))
     return out
+
+
+def grouped_gemm(stage: int, ids: np.ndarray, E: int, a, w0, w1=None, *, a_scale=None, s0=None, s1=None,
+                 ep_size: int = 1, ep_rank: int = 0) -> np.ndarray:
+    """One grouped GEMM stage (oracle.c oracle_grouped_gemm) -> float64 [R, N] in grouped order.
+
+    ids [T,k] int32 (grouped as route_permute does); stage 0: a [T,H] activation rows, w0/w1 gate
+    and up [E_loc,I,H]; stage 1: a [T*k,I] grouped rows (first R used), w0 down [E_loc,H,I].
+    a: uint16 bf16 bits, or uint8 e4m3 codes with a_scale [rows, K/128]; weights: uint16 bf16 bits,
+    or uint8 codes with block scales s0 (and s1 for up)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    a_fp8 = a.dtype == np.uint8
+    a = _c(a, np.uint8 if a_fp8 else np.uint16)
+    K = a.shape[1]
+    w_fp8 = w0.dtype == np.uint8
+    wdt = np.uint8 if w_fp8 else np.uint16
+    w0 = _c(w0, wdt)
+    N = w0.shape[1]
+    w1 = _c(w1, wdt) if stage == 0 else w0
+    a_scale = _c(a_scale, np.float32) if a_fp8 else np.zeros(1, np.float32)
+    if w_fp8:
+        s0 = _c(s0, np.float32)
+        s1 = _c(s1, np.float32) if stage == 0 else s0
+    else:
+        s0 = s1 = np.zeros(1, np.float32)
+    out = np.zeros((max(T * k, 1), N), np.float64)
+    R = _load().oracle_grouped_gemm(stage, T, k, E, ep_size, ep_rank, N, K, int(a_fp8), _p(ids), _p(a),
+                                    _p(a_scale), int(w_fp8), _p(w0), _p(w1), _p(s0), _p(s1), _p(out))
+    return out[:R].copy()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel loops (n <= 0 leaves the setting)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:

@@ -400,6 +400,63 @@ void oracle_moe_tokens(int T, int H, int I, int E, int k, int ep_size, int ep_ra
     }
 }
 
+/* One grouped GEMM stage of the layer on given operands, rows in the grouped order of
+ * oracle_route_permute (local experts ascending, flat index ascending inside an expert):
+ *   stage 0 (gate/up): grouped row p of flat assignment i = perm_src[p], token t = i / k,
+ *     local expert l:  g_n = sum_h a[t,h] Wg[l,n,h],  u_n = sum_h a[t,h] Wu[l,n,h],
+ *     out[p,n] = g_n / (1 + exp(-g_n)) * u_n       (SiLU on the gate times up; n < N = I)
+ *   stage 1 (down): out[p,n] = sum_i a[p,i] Wd[l,n,i]  (n < N = H; a holds grouped rows)
+ * a is bf16 (a_fp8 = 0: uint16 bit patterns) or e4m3 codes times the fp32 scale of their
+ * 128-column group (a_fp8 = 1: a_scale [rows, K/128]); weights as in oracle_moe_tokens
+ * (w1/s1 unused in stage 1).  Double arithmetic, sums in ascending reduction index.  Writes
+ * out[0..R-1] ([R, N], R = local rows) and returns R. */
+int oracle_grouped_gemm(int stage, int T, int k, int E, int ep_size, int ep_rank, int N, int K, int a_fp8,
+                        const int32_t* ids, const void* a, const float* a_scale, int w_fp8, const void* w0,
+                        const void* w1, const float* s0, const float* s1, double* out) {
+    int El = E / ep_size;
+    long long n = (long long)T * k;
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)(El > 0 ? El : 1));
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(El + 1));
+    int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    oracle_route_permute(T, k, E, ep_size, ep_rank, ids, counts, offsets, perm, inv, NULL);
+    int R = offsets[El];
+    int G = K / 128;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int p = 0; p < R; p++) {
+        int l = 0;
+        while (offsets[l + 1] <= p) l++; /* the expert whose rows hold p */
+        int row = (stage == 0) ? perm[p] / k : p;
+        double* av = (double*)malloc(sizeof(double) * (size_t)K);
+        for (int c = 0; c < K; c++) {
+            size_t idx = (size_t)row * K + c;
+            av[c] = a_fp8 ? (double)oracle_e4m3_decode(((const uint8_t*)a)[idx]) * (double)a_scale[(size_t)row * G + c / 128]
+                          : (double)oracle_bf16_to_f32(((const uint16_t*)a)[idx]);
+        }
+        for (int f = 0; f < N; f++) {
+            double acc0 = 0.0, acc1 = 0.0;
+            for (int c = 0; c < K; c++) {
+                acc0 += av[c] * wval(w0, s0, w_fp8, l, f, c, N, K);
+                if (stage == 0) acc1 += av[c] * wval(w1, s1, w_fp8, l, f, c, N, K);
+            }
+            out[(size_t)p * N + f] = (stage == 0) ? acc0 / (1.0 + exp(-acc0)) * acc1 : acc0;
+        }
+        free(av);
+    }
+    free(counts); free(offsets); free(perm); free(inv);
+    return R;
+}
+
+/* Thread count of the OpenMP loops above (the benchmark times the oracle on one core and on
+ * all of them); 0 or less keeps the current setting. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads OpenMP would use for oracle_moe_tokens (reported beside its timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -450,3 +450,87 @@ def test_grouped_router_rejects_impossible_shapes():
     for k, ng, tg in ((3, 5, 2), (3, 4, 0), (3, 4, 5), (7, 4, 2)):
         with pytest.raises(ValueError):
             oracle.router_topk_grouped(lg, k, ng, tg)
+
+
+# ----------------------------------------------------------------------------- grouped GEMM stage
+
+def _grouped_rows(ids, E, ep_size, ep_rank):
+    """(flat assignment, local expert) of each grouped row, from NumPy's stable argsort (no oracle)."""
+    El = E // ep_size
+    flat = ids.reshape(-1).astype(np.int64)
+    loc = flat - ep_rank * El
+    ok = (flat >= 0) & (flat < E) & (loc >= 0) & (loc < El)
+    idx = np.nonzero(ok)[0]
+    order = idx[np.argsort(loc[idx], kind="stable")]
+    return order, loc[order]
+
+
+@pytest.mark.parametrize("fp8,ep_size,ep_rank", [(False, 1, 0), (False, 2, 1), (True, 1, 0), (True, 4, 3)])
+def test_grouped_gemm_matches_numpy_matmuls(fp8, ep_size, ep_rank):
+    """Both stages against float64 NumPy matmuls over NumPy's stable grouping: random ids with
+    repeats, out-of-range ids and other ranks' experts; FP8 operands decoded by torch's e4m3."""
+    T, H, I, E, k = 23, 256, 384, 8, 3
+    L = synth.tiny_layer(T, H, E // ep_size, I, seed=21)
+    g = np.random.default_rng(22)
+    ids = g.integers(-2, E + 2, (T, k)).astype(np.int32)
+    ids[0] = [1, 1, 1]
+    order, loc = _grouped_rows(ids, E, ep_size, ep_rank)
+    R = len(order)
+    if fp8:
+        qs = [synth.block_quantize_fp8(L[n]) for n in ("wg", "wu", "wd")]
+        (qg, sg), (qu, su), (qd, sd) = qs
+
+        def deq(q, s):
+            return (q.view(torch.float8_e4m3fn).double() *
+                    s.double().repeat_interleave(128, 1).repeat_interleave(128, 2)).numpy()
+        Wg, Wu, Wd = deq(qg, sg), deq(qu, su), deq(qd, sd)
+        xq = g.integers(0, 0x7F, (T, H)).astype(np.uint8)        # every finite positive code
+        xq[g.random((T, H)) < 0.5] |= 0x80                        # and its negative
+        xs = g.uniform(0.25, 4.0, (T, H // 128)).astype(np.float32)
+        xv = torch.from_numpy(xq).view(torch.float8_e4m3fn).double().numpy() * np.repeat(xs, 128, 1)
+        out0 = oracle.grouped_gemm(0, ids, E, xq, qg.numpy(), qu.numpy(), a_scale=xs, s0=sg.numpy(), s1=su.numpy(),
+                                   ep_size=ep_size, ep_rank=ep_rank)
+        hq = g.integers(0, 0x7F, (T * k, I)).astype(np.uint8)
+        hs = g.uniform(0.25, 4.0, (T * k, I // 128)).astype(np.float32)
+        hv = torch.from_numpy(hq).view(torch.float8_e4m3fn).double().numpy() * np.repeat(hs, 128, 1)
+        out1 = oracle.grouped_gemm(1, ids, E, hq, qd.numpy(), a_scale=hs, s0=sd.numpy(), ep_size=ep_size,
+                                   ep_rank=ep_rank)
+    else:
+        Wg, Wu, Wd = (L[n].double().numpy() for n in ("wg", "wu", "wd"))
+        xv = L["x"].double().numpy()
+        out0 = oracle.grouped_gemm(0, ids, E, synth.bf16_bits(L["x"]), synth.bf16_bits(L["wg"]),
+                                   synth.bf16_bits(L["wu"]), ep_size=ep_size, ep_rank=ep_rank)
+        hb = torch.from_numpy(g.standard_normal((T * k, I)).astype(np.float32)).to(torch.bfloat16)
+        hv = hb.double().numpy()
+        out1 = oracle.grouped_gemm(1, ids, E, synth.bf16_bits(hb), synth.bf16_bits(L["wd"]), ep_size=ep_size,
+                                   ep_rank=ep_rank)
+    assert out0.shape == (R, I) and out1.shape == (R, H)
+    tok = order // k
+    gg = np.einsum("rh,rnh->rn", xv[tok], Wg[loc])
+    uu = np.einsum("rh,rnh->rn", xv[tok], Wu[loc])
+    ref0 = gg / (1.0 + np.exp(-gg)) * uu
+    ref1 = np.einsum("ri,rhi->rh", hv[:R], Wd[loc])
+    assert np.allclose(out0, ref0, rtol=1e-11, atol=1e-12)
+    assert np.allclose(out1, ref1, rtol=1e-11, atol=1e-12)
+
+
+def test_grouped_gemm_on_integer_data_is_exact():
+    """Integer operands give integer sums: the stage equals exact int64 matmuls (gate sums kept
+    large, where silu(g) = g in double), with a whole empty expert."""
+    T, H, I, E, k = 40, 128, 256, 6, 2
+    g = np.random.default_rng(23)
+    ids = g.integers(0, E - 1, (T, k)).astype(np.int32)  # expert E-1 stays empty
+    x = g.integers(1, 3, (T, H))
+    wg = g.integers(1, 3, (E, I, H))
+    wu = g.integers(-2, 3, (E, I, H))
+    wd = g.integers(-2, 3, (E, H, I))
+    h = g.integers(-2, 3, (T * k, I))
+    bits = lambda a: synth.bf16_bits(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16))
+    out0 = oracle.grouped_gemm(0, ids, E, bits(x), bits(wg), bits(wu))
+    out1 = oracle.grouped_gemm(1, ids, E, bits(h), bits(wd))
+    order, loc = _grouped_rows(ids, E, 1, 0)
+    gi = np.einsum("rh,rnh->rn", x[order // k], wg[loc])
+    ui = np.einsum("rh,rnh->rn", x[order // k], wu[loc])
+    assert gi.min() >= H  # exp(-g) < 2^-60: silu(g) == g exactly in double
+    assert np.array_equal(out0, (gi * ui).astype(np.float64))
+    assert np.array_equal(out1, np.einsum("ri,rhi->rh", h[:len(order)], wd[loc]).astype(np.float64))
