@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define FMOE_ABI_VERSION 2
+#define FMOE_ABI_VERSION 3
 
 /* Limits of the library (checked, FMOE_ERR_UNSUPPORTED beyond them). */
 #define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
@@ -138,8 +138,10 @@ int fmoe_router_topk_grouped(const void* logits, int32_t logits_dtype, int32_t T
                              int32_t n_group, int32_t topk_group, int32_t scoring, int32_t renormalize,
                              int32_t* topk_ids, float* topk_weights, void* stream);
 
-/* Per-expert grouping of the T*k assignments topk_ids [T,k] for this rank (shape gives
- * T, E, k, ep_size, ep_rank; H, I and weight_dtype are used only to size the workspace):
+/* Per-expert grouping of the T*k assignments topk_ids [T,k] for this rank.  [H20] paragraph
+ * 3: the kernel and tile choice need the rows assigned to each expert, not the token count;
+ * [PR39593] Root cause: repeated ids in one token must not break the expert kernels.
+ * (shape gives T, E, k, ep_size, ep_rank; H, I and weight_dtype only size the workspace):
  *   counts [E_loc]      rows per local expert
  *   offsets [E_loc+1]   exclusive prefix sum of counts, offsets[E_loc] = R
  *   perm_src [T*k]      first R entries: flat index t*k+j of each grouped row, experts
@@ -151,7 +153,10 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
                        int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
                        void* ws, size_t ws_bytes, void* stream);
 
-/* Expert computation for given routing: out[t,:] = sum over j ascending with a local id of
+/* Expert computation for given routing ([H20] paragraph 2: a fused-experts call that takes the
+ * routing, the expert-parallel size and rank and FP8 block scales; [LAB6] intro: w8a8 with
+ * [128,128] weight blocks; [PR39593] Root cause: repeated ids, and the e4m3 clamp to +-448):
+ *   out[t,:] = sum over j ascending with a local id of
  *   topk_weights[t,j] * W_down[l] (silu(W_gate[l] x[t]) * (W_up[l] x[t])),  l = id - ep_rank*E_loc,
  * computed as grouping -> (FP8: per-token per-128 e4m3 quantisation of x) -> grouped gate/up
  * GEMM with fused SiLU-and-mul -> (FP8: quantisation of the activation) -> grouped down GEMM ->
@@ -162,8 +167,10 @@ int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids
                  const float* topk_weights, const fmoe_weights* w, void* out,
                  void* ws, size_t ws_bytes, void* stream);
 
-/* Whole layer: fmoe_router_topk on logits [T,E] then fmoe_experts.  topk_ids_out [T,k] and
- * topk_weights_out [T,k] receive the routing when not NULL (otherwise it stays in ws). */
+/* Whole layer: the router of [PR39593] Fix (fmoe_router_topk) on logits [T,E], then the
+ * expert computation of [H20] paragraph 2 (fmoe_experts), with the tile plan from the
+ * rows-per-expert estimate of [H20] paragraph 3.  topk_ids_out [T,k] and topk_weights_out
+ * [T,k] receive the routing when not NULL (otherwise it stays in ws). */
 int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype,
                  int32_t scoring, int32_t renormalize, const fmoe_weights* w, void* out,
                  int32_t* topk_ids_out, float* topk_weights_out, void* ws, size_t ws_bytes,
@@ -199,6 +206,53 @@ int fmoe_forward_planned(const fmoe_shape* shape, const void* x, const void* log
                          const fmoe_weights* w, void* out, int32_t* topk_ids_out,
                          float* topk_weights_out, void* ws, size_t ws_bytes, void* stream,
                          const fmoe_plan* plan);
+
+/* Per-row, per-128-column e4m3 quantisation of activations (the w8a8 activation scheme of
+ * [LAB6] intro; the saturating fminf/fmaxf clamp of [PR39593] Root cause), the code the
+ * layer runs on x and on the gate/up activation:
+ *   for every row r and group g of 128 columns: amax = max |x| over the group (NaN ignored);
+ *   s[r,g] = amax/448 (1 when amax == 0); inv = 1/s; q = e4m3(max(min(x*inv, 448), -448))
+ *   (round to nearest even; a NaN value becomes +448).  IEEE fp32 division and product.
+ *   x [rows, cols] bf16 (x_dtype FMOE_BF16) or fp32 (FMOE_FP32) -> q [rows, cols] e4m3 codes,
+ *   s [rows, cols/128] fp32.  cols a positive multiple of 128, at most FMOE_MAX_DIM;
+ *   rows >= 0 (0: no-op); x, q 16-byte aligned. */
+int fmoe_act_quant(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q, float* s,
+                   void* stream);
+
+/* Byte offsets of the layer's intermediate buffers inside a workspace of
+ * fmoe_workspace_bytes(shape) bytes, for tests and inspection (0: the buffer does not exist
+ * for this weight dtype).  After fmoe_forward / fmoe_experts on ws (stream synchronised):
+ *   x_codes [T,H] e4m3, x_scales [T,H/128] fp32 (FP8): the quantised x;
+ *   h_f32 [T*k,I] fp32 (FP8): the gate/up activation of grouped row p, when the layer
+ *       quantised it in a separate pass (some expert could take a heavy row tile);
+ *   h_codes [T*k,I] e4m3, h_scales [T*k,I/128] fp32 (FP8): the quantised activation;
+ *   h_bf16 [T*k,I] bf16 (bf16 weights): the activation;
+ *   y [T*k,H] bf16: the down projection of grouped row p (before the routing weight);
+ *   perm_src, inv_perm [T*k] int32: the grouping (as fmoe_route_permute).
+ * Only the first R grouped rows (fmoe_read_stats local_rows) hold data. */
+typedef struct {
+    size_t x_codes, x_scales, h_f32, h_codes, h_scales, h_bf16, y, perm_src, inv_perm, total;
+} fmoe_layout;
+int fmoe_workspace_layout(const fmoe_shape* shape, fmoe_layout* out);
+
+/* One grouped GEMM stage of fmoe_experts on operands the caller gives, for tests of the GEMM
+ * kernels (integer data makes every kernel's result exact) and for tuning.  topk_ids [T,k]
+ * are grouped as fmoe_route_permute does (caller ids: repeats legal, out-of-range dropped),
+ * the row tiles are cut from the real counts with the tile plan (*plan, NULL: the heuristic;
+ * fields as for fmoe_forward_planned), and the kernels fmoe_experts would launch run:
+ *   stage 0 (gate/up): a = activation rows [T,H]: bf16, or e4m3 codes with a_scale [T,H/128];
+ *     grouped row p (token t = perm_src[p] / k, local expert l) gets
+ *     silu(a[t] . W_gate[l]^T) * (a[t] . W_up[l]^T) in out [T*k, I] as
+ *       out_dtype FMOE_BF16 (bf16 weights), FMOE_FP32 (FP8 weights), or FMOE_FP8_E4M3 (FP8
+ *       weights: codes, with out_scale [T*k, I/128] as fmoe_act_quant computes them);
+ *   stage 1 (down): a = grouped rows [T*k, I]: bf16, or codes with a_scale [T*k, I/128];
+ *     out [T*k, H] bf16: row p = a[p] . W_down[l]^T  (out_dtype FMOE_BF16).
+ * FP8 operands are used as code * scale per 128-deep block (weights per [128,128] block).
+ * Rows p >= R are not written.  ws: fmoe_workspace_bytes(shape) bytes.  Errors as
+ * fmoe_experts; FMOE_ERR_ARG for a stage or out_dtype that does not fit the weights. */
+int fmoe_grouped_gemm(const fmoe_shape* shape, const fmoe_plan* plan, int32_t stage, const int32_t* topk_ids,
+                      const void* a, const float* a_scale, const fmoe_weights* w, int32_t out_dtype, void* out,
+                      float* out_scale, void* ws, size_t ws_bytes, void* stream);
 
 /* Stages of fmoe_forward, in launch order, for fmoe_forward_profiled. */
 enum {

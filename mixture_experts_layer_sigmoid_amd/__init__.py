@@ -23,7 +23,8 @@ FMOE_NUM_STAGES = 9
 STAGES = ("router", "group", "quant_x", "gemm1", "gemm1_heavy", "quant_h", "gemm2", "gemm2_heavy", "combine")
 EXPORTED = ("fmoe_abi_version", "fmoe_status_string", "fmoe_workspace_bytes", "fmoe_router_logits",
             "fmoe_router_topk", "fmoe_route_permute", "fmoe_experts", "fmoe_forward", "fmoe_forward_profiled",
-            "fmoe_forward_planned", "fmoe_router_topk_grouped", "fmoe_read_stats")
+            "fmoe_forward_planned", "fmoe_router_topk_grouped", "fmoe_read_stats", "fmoe_act_quant",
+            "fmoe_workspace_layout", "fmoe_grouped_gemm")
 
 
 class fmoe_shape(ctypes.Structure):
@@ -43,6 +44,12 @@ class fmoe_plan(ctypes.Structure):
     tiles per expert at most (8: heavy-tile launches left out when no expert can need more)."""
     _fields_ = [("tile_rows", ctypes.c_int32), ("split_gate_up", ctypes.c_int32), ("split_down", ctypes.c_int32),
                 ("light_tiles", ctypes.c_int32)]
+
+
+class fmoe_layout(ctypes.Structure):
+    """Byte offsets of the intermediate buffers inside a workspace (0: absent for this dtype)."""
+    _fields_ = [(n, ctypes.c_size_t) for n in ("x_codes", "x_scales", "h_f32", "h_codes", "h_scales", "h_bf16",
+                                               "y", "perm_src", "inv_perm", "total")]
 
 
 class fmoe_stats(ctypes.Structure):
@@ -79,6 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmoe_forward_profiled.argtypes = lib.fmoe_forward.argtypes + [P]
     lib.fmoe_forward_planned.argtypes = lib.fmoe_forward.argtypes + [ctypes.POINTER(fmoe_plan)]
     lib.fmoe_read_stats.argtypes = [P, P, ctypes.POINTER(fmoe_stats)]
+    lib.fmoe_act_quant.argtypes = [P, i32, ctypes.c_int64, i32, P, P, P]
+    lib.fmoe_workspace_layout.argtypes = [ctypes.POINTER(fmoe_shape), ctypes.POINTER(fmoe_layout)]
+    lib.fmoe_grouped_gemm.argtypes = [ctypes.POINTER(fmoe_shape), ctypes.POINTER(fmoe_plan), i32, P, P, P,
+                                      ctypes.POINTER(fmoe_weights), i32, P, P, P, sz, P]
     for name in EXPORTED:
         if name != "fmoe_status_string":
             getattr(lib, name).restype = ctypes.c_int
@@ -297,3 +308,63 @@ def fmoe_read_stats(ws: torch.Tensor) -> dict:
     st = fmoe_stats()
     _check("fmoe_read_stats", load_library().fmoe_read_stats(_ptr(ws), _stream(ws.device), ctypes.byref(st)))
     return {name: getattr(st, name) for name, _ in fmoe_stats._fields_}
+
+
+def fmoe_act_quant(x: torch.Tensor):
+    """Per-row, per-128-column e4m3 quantisation: x [rows, cols] bf16 or fp32 -> (codes uint8
+    [rows, cols], scales fp32 [rows, cols/128])."""
+    _dev(x, "x")
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    sc = torch.empty((rows, max(cols // 128, 1)), dtype=torch.float32, device=x.device)
+    _check("fmoe_act_quant", load_library().fmoe_act_quant(_ptr(x), _dtype_code(x), rows, cols, _ptr(q), _ptr(sc),
+                                                           _stream(x.device)))
+    return q, sc
+
+
+def fmoe_workspace_layout(shape: fmoe_shape) -> dict:
+    """Byte offsets of the layer's intermediate buffers in a workspace of this shape (0: absent)."""
+    lay = fmoe_layout()
+    _check("fmoe_workspace_layout", load_library().fmoe_workspace_layout(ctypes.byref(shape), ctypes.byref(lay)))
+    return {name: int(getattr(lay, name)) for name, _ in fmoe_layout._fields_}
+
+
+def ws_view(ws: torch.Tensor, offset: int, dtype, shape) -> torch.Tensor:
+    """A typed view of `shape` elements at byte `offset` of a uint8 workspace tensor."""
+    n = 1
+    for d in shape:
+        n *= int(d)
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return ws[offset:offset + nbytes].view(dtype).view(*shape)
+
+
+def fmoe_grouped_gemm(shape: fmoe_shape, stage: int, topk_ids: torch.Tensor, a: torch.Tensor, w: ExpertWeights,
+                      a_scale: torch.Tensor | None = None, out_dtype: int | None = None,
+                      plan: fmoe_plan | None = None, ws: torch.Tensor | None = None):
+    """One grouped GEMM stage on given operands (rows in grouped order, T*k of them allocated).
+    stage 0 -> out [T*k, I] (bf16 weights: bf16; FP8: fp32, or (codes, scales) for out_dtype
+    FMOE_FP8_E4M3); stage 1 -> out [T*k, H] bf16."""
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(a, "a")
+    if a_scale is not None:
+        _dev(a_scale, "a_scale", torch.float32)
+    dev = a.device
+    n = max(shape.tokens * shape.top_k, 1)
+    if out_dtype is None:
+        out_dtype = FMOE_FP32 if (w.fp8 and stage == 0) else FMOE_BF16
+    N = shape.inter if stage == 0 else shape.hidden
+    out_scale = None
+    if out_dtype == FMOE_FP32:
+        out = torch.empty((n, N), dtype=torch.float32, device=dev)
+    elif out_dtype == FMOE_FP8_E4M3:
+        out = torch.empty((n, N), dtype=torch.uint8, device=dev)
+        out_scale = torch.empty((n, N // 128), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty((n, N), dtype=torch.bfloat16, device=dev)
+    ws = workspace(shape, dev) if ws is None else ws
+    ws_struct = w.struct()
+    _check("fmoe_grouped_gemm",
+           load_library().fmoe_grouped_gemm(ctypes.byref(shape), None if plan is None else ctypes.byref(plan), stage,
+                                            _ptr(topk_ids), _ptr(a), _ptr(a_scale), ctypes.byref(ws_struct), out_dtype,
+                                            _ptr(out), _ptr(out_scale), _ptr(ws), ws.numel(), _stream(dev)))
+    return (out, out_scale) if out_dtype == FMOE_FP8_E4M3 else out

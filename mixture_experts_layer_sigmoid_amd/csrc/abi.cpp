@@ -16,6 +16,8 @@
 
 #include <climits>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/fmoe.h"
@@ -197,6 +199,26 @@ int device_cus() {
     return cache[dev];
 }
 
+// FMOE_LOG=1 in the environment (read once): every layer call prints its plan to stderr, one
+// line, before it launches anything.
+bool log_enabled() {
+    static const int on = [] {
+        const char* v = std::getenv("FMOE_LOG");
+        return (v && *v && std::strcmp(v, "0") != 0) ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+void log_plan(const char* who, const Plan& p) {
+    if (!log_enabled()) return;
+    std::fprintf(stderr,
+                 "[fmoe] %s: T=%d H=%d I=%d E=%d k=%d E_loc=%d first_expert=%d %s | rows_estimate=%d "
+                 "tile_rows=%d light_cap=%d heavy_launch=%d heavy_rows=%d split_gate_up=%d split_down=%d "
+                 "max_light_tiles=%d max_heavy_tiles=%d workspace=%zu B\n",
+                 who, p.T, p.H, p.I, p.E, p.k, p.El, p.lo, p.fp8 ? "fp8" : "bf16", p.rows_estimate, p.tile_rows,
+                 p.light_cap, (int)p.heavy_launch, p.heavy_rows, p.wk1, p.wk2, p.max_light, p.max_heavy, p.L.total);
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FMOE_OK : FMOE_ERR_HIP; }
 
 #define FMOE_TRY(expr)                          \
@@ -306,6 +328,70 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     return FMOE_OK;
 }
 
+// One GEMM stage of run_experts on caller operands (fmoe_grouped_gemm): grouping of ids, then
+// the light and heavy launches of that stage.  stage 0: a = [T, H] rows gathered through
+// perm_src, out [n, I]; stage 1: a = [n, I] grouped rows, out [n, H] bf16.  out_mode for
+// stage 0: kOutBf16 (bf16), kOutF32 or kOutE4M3 (FP8: fused into the streaming kernel when it
+// alone runs, else the fp32 activation in ws.h and then the quantisation kernel).
+int run_stage(const Plan& p, int stage, const int32_t* ids, const void* a, const float* a_scale,
+              const fmoe_weights* w, int out_mode, void* out, float* out_scale, char* ws, hipStream_t st) {
+    const Layout& L = p.L;
+    DevHeader* hdr = (DevHeader*)(ws + L.hdr);
+    int32_t* perm = (int32_t*)(ws + L.perm);
+    MTile* mtiles = (MTile*)(ws + L.mtiles);
+    MTile* mtiles_heavy = mtiles + p.max_light;
+    const int cus = device_cus();
+    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate,
+                          (int32_t*)(ws + L.counts), (int32_t*)(ws + L.offsets), perm, (int32_t*)(ws + L.inv),
+                          (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles, mtiles_heavy, hdr, st));
+    GemmArgs g;
+    g.A = a;
+    g.A_scale = p.fp8 ? a_scale : nullptr;
+    g.topk = p.k;
+    g.out_scale = nullptr;
+    g.mtiles = mtiles;
+    g.tile_count = &hdr->m_tiles;
+    if (stage == 0) {
+        g.perm_src = perm;
+        g.W0 = w->gate;
+        g.W1 = w->up;
+        g.S0 = w->gate_scale;
+        g.S1 = w->up_scale;
+        g.N = p.I;
+        g.K = p.H;
+        const bool fused = out_mode == kOutE4M3 && !p.heavy_launch && p.wk1 == 1;
+        const bool via_f32 = out_mode == kOutE4M3 && !fused;
+        g.out = via_f32 ? (void*)(ws + L.h) : out;
+        g.out_scale = fused ? out_scale : nullptr;
+        GemmArgs gh = g;
+        gh.mtiles = mtiles_heavy;
+        gh.tile_count = &hdr->m_tiles_heavy;
+        const bool f32 = p.fp8;  // FP8 writes fp32 (or codes), bf16 writes bf16
+        if (p.wk1 == 1)
+            FMOE_TRY(launch_grouped_gemm_stream(true, p.fp8, fused ? kOutE4M3 : f32 ? kOutF32 : kOutBf16, g,
+                                                p.tile_rows, p.max_light, cus, st));
+        else FMOE_TRY(launch_grouped_gemm(true, p.fp8, f32, g, p.tile_rows, p.wk1, p.max_light, cus, st));
+        if (p.heavy_launch) FMOE_TRY(launch_grouped_gemm_tiled(true, p.fp8, f32, gh, p.max_heavy, cus, st));
+        if (via_f32) FMOE_TRY(launch_quant_rows(ws + L.h, false, p.n, p.I, (uint8_t*)out, out_scale, hdr, st));
+        return FMOE_OK;
+    }
+    g.perm_src = nullptr;
+    g.W0 = w->down;
+    g.W1 = nullptr;
+    g.S0 = w->down_scale;
+    g.S1 = nullptr;
+    g.N = p.H;
+    g.K = p.I;
+    g.out = out;
+    GemmArgs gh = g;
+    gh.mtiles = mtiles_heavy;
+    gh.tile_count = &hdr->m_tiles_heavy;
+    if (p.wk2 == 1) FMOE_TRY(launch_grouped_gemm_stream(false, p.fp8, kOutBf16, g, p.tile_rows, p.max_light, cus, st));
+    else FMOE_TRY(launch_grouped_gemm(false, p.fp8, false, g, p.tile_rows, p.wk2, p.max_light, cus, st));
+    if (p.heavy_launch) FMOE_TRY(launch_grouped_gemm_tiled(false, p.fp8, false, gh, p.max_heavy, cus, st));
+    return FMOE_OK;
+}
+
 // Values a tile plan may force; the FP8 split kernel's LDS limit for 32-row tiles.
 int check_plan(const fmoe_shape* s, const fmoe_plan* ov) {
     if (!ov) return FMOE_OK;
@@ -333,6 +419,7 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
     if (!x || !logits || !out || !ws) return FMOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return FMOE_ERR_ARG;
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
+    log_plan(ov ? "fmoe_forward_planned" : "fmoe_forward", p);
     hipStream_t st = (hipStream_t)stream;
     char* wsb = (char*)ws;
     int32_t* ids = ids_out ? ids_out : (int32_t*)(wsb + p.L.ids);
@@ -444,6 +531,7 @@ int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids
     if (!x || !topk_ids || !topk_weights || !out || !ws) return FMOE_ERR_ARG;
     if (!aligned16(x) || !aligned16(out) || !aligned16(ws)) return FMOE_ERR_ARG;
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
+    log_plan("fmoe_experts", p);
     return run_experts(p, x, topk_ids, topk_weights, w, out, (char*)ws, (hipStream_t)stream, nullptr);
 }
 
@@ -469,6 +557,71 @@ int fmoe_forward_planned(const fmoe_shape* shape, const void* x, const void* log
                          const fmoe_plan* plan) {
     return forward_impl(shape, x, logits, logits_dtype, scoring, renormalize, w, out, topk_ids_out,
                         topk_weights_out, ws, ws_bytes, stream, nullptr, plan);
+}
+
+int fmoe_act_quant(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, uint8_t* q, float* s, void* stream) {
+    if (rows < 0 || cols <= 0) return FMOE_ERR_ARG;
+    if (cols % 128 || cols > FMOE_MAX_DIM) return FMOE_ERR_UNSUPPORTED;
+    if (x_dtype != FMOE_BF16 && x_dtype != FMOE_FP32) return FMOE_ERR_UNSUPPORTED;
+    if (rows * (cols / 128) > (long long)INT_MAX * 4) return FMOE_ERR_UNSUPPORTED;  // grid size
+    if (rows == 0) return FMOE_OK;
+    if (!x || !q || !s) return FMOE_ERR_ARG;
+    if (!aligned16(x) || !aligned16(q) || ((uintptr_t)s & 3u)) return FMOE_ERR_ARG;
+    return hip_status(launch_quant_rows(x, x_dtype == FMOE_BF16, rows, cols, q, s, nullptr, (hipStream_t)stream));
+}
+
+int fmoe_workspace_layout(const fmoe_shape* shape, fmoe_layout* out) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!out) return FMOE_ERR_ARG;
+    const Plan p = make_plan(shape);
+    const Layout& L = p.L;
+    std::memset(out, 0, sizeof(*out));
+    if (p.fp8) {
+        out->x_codes = L.xq;
+        out->x_scales = L.xs;
+        out->h_f32 = L.h;
+        out->h_codes = L.hq;
+        out->h_scales = L.hs;
+    } else {
+        out->h_bf16 = L.h;
+    }
+    out->y = L.y;
+    out->perm_src = L.perm;
+    out->inv_perm = L.inv;
+    out->total = L.total;
+    return FMOE_OK;
+}
+
+int fmoe_grouped_gemm(const fmoe_shape* shape, const fmoe_plan* plan, int32_t stage, const int32_t* topk_ids,
+                      const void* a, const float* a_scale, const fmoe_weights* w, int32_t out_dtype, void* out,
+                      float* out_scale, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_plan(shape, plan))) return rc;
+    if (stage != 0 && stage != 1) return FMOE_ERR_ARG;
+    Plan p = make_plan(shape, plan);
+    if ((rc = check_weights(p, w))) return rc;
+    int mode;
+    if (stage == 1) {
+        if (out_dtype != FMOE_BF16) return FMOE_ERR_ARG;
+        mode = kOutBf16;
+    } else if (!p.fp8) {
+        if (out_dtype != FMOE_BF16) return FMOE_ERR_ARG;
+        mode = kOutBf16;
+    } else {
+        if (out_dtype == FMOE_FP32) mode = kOutF32;
+        else if (out_dtype == FMOE_FP8_E4M3) mode = kOutE4M3;
+        else return FMOE_ERR_ARG;
+    }
+    if (p.T == 0) return FMOE_OK;
+    if (!topk_ids || !a || !out || !ws) return FMOE_ERR_ARG;
+    if (p.fp8 && !a_scale) return FMOE_ERR_ARG;
+    if (mode == kOutE4M3 && !out_scale) return FMOE_ERR_ARG;
+    if (!aligned16(a) || !aligned16(out) || !aligned16(ws)) return FMOE_ERR_ARG;
+    if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
+    log_plan(stage == 0 ? "fmoe_grouped_gemm gate/up" : "fmoe_grouped_gemm down", p);
+    return run_stage(p, stage, topk_ids, a, a_scale, w, mode, out, out_scale, (char*)ws, (hipStream_t)stream);
 }
 
 int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {

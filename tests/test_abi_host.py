@@ -28,9 +28,9 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = fm.load_library()
-    assert fm.fmoe_abi_version() == 2
+    assert fm.fmoe_abi_version() == 3
     text = open(HEADER).read()
-    assert "#define FMOE_ABI_VERSION 2" in text
+    assert "#define FMOE_ABI_VERSION 3" in text
     for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")]:
         assert word in lib.fmoe_status_string(code)
 
@@ -164,3 +164,56 @@ def test_grouped_router_rejects_bad_groups_before_launching():
     assert call(64, 9, 8, 1) == fm.FMOE_ERR_ARG        # 8 experts in one kept group < k
     assert call(256, 4, 128, 2) == fm.FMOE_ERR_UNSUPPORTED  # more than 64 groups
     assert lib.fmoe_router_topk_grouped(P(0x100), 0, 0, 64, 4, 8, 2, 0, 1, None, None, None) == fm.FMOE_OK  # T = 0
+
+
+def test_quantisation_and_grouped_gemm_reject_bad_arguments_without_a_device():
+    lib = fm.load_library()
+    P = ctypes.c_void_p
+    # fmoe_act_quant: cols not a multiple of 128, unsupported dtype, null or misaligned buffers
+    assert lib.fmoe_act_quant(P(0x100), fm.FMOE_BF16, 4, 200, P(0x200), P(0x300), None) == fm.FMOE_ERR_UNSUPPORTED
+    assert lib.fmoe_act_quant(P(0x100), fm.FMOE_FP8_E4M3, 4, 256, P(0x200), P(0x300), None) == fm.FMOE_ERR_UNSUPPORTED
+    assert lib.fmoe_act_quant(None, fm.FMOE_BF16, 4, 256, P(0x200), P(0x300), None) == fm.FMOE_ERR_ARG
+    assert lib.fmoe_act_quant(P(0x108), fm.FMOE_BF16, 4, 256, P(0x200), P(0x300), None) == fm.FMOE_ERR_ARG
+    assert lib.fmoe_act_quant(P(0x100), fm.FMOE_BF16, -1, 256, P(0x200), P(0x300), None) == fm.FMOE_ERR_ARG
+    assert lib.fmoe_act_quant(None, fm.FMOE_BF16, 0, 256, None, None, None) == fm.FMOE_OK  # no rows: no-op
+    # fmoe_grouped_gemm: bad stage, output dtype that does not fit the weights, missing scales
+    s = fm.make_shape(16, 256, 128, 8, 2)
+    w = fm.fmoe_weights(0x1000, 0x2000, 0x3000, None, None, None)
+    n = fm.fmoe_workspace_bytes(s)
+
+    def gg(shape, weights, stage, out_dtype, a_scale=None, out_scale=None, ws_n=None):
+        return lib.fmoe_grouped_gemm(ctypes.byref(shape), None, stage, P(0x100), P(0x200), a_scale,
+                                     ctypes.byref(weights), out_dtype, P(0x300), out_scale, P(0x400),
+                                     n if ws_n is None else ws_n, None)
+    assert gg(s, w, 2, fm.FMOE_BF16) == fm.FMOE_ERR_ARG
+    assert gg(s, w, 0, fm.FMOE_FP32) == fm.FMOE_ERR_ARG          # bf16 weights write bf16
+    assert gg(s, w, 1, fm.FMOE_FP8_E4M3) == fm.FMOE_ERR_ARG
+    assert gg(s, w, 0, fm.FMOE_BF16, ws_n=n - 1) == fm.FMOE_ERR_WORKSPACE
+    s8 = fm.make_shape(16, 256, 128, 8, 2, fp8=True)
+    w8 = fm.fmoe_weights(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
+    n = fm.fmoe_workspace_bytes(s8)
+    assert gg(s8, w8, 0, fm.FMOE_BF16, a_scale=P(0x500)) == fm.FMOE_ERR_ARG       # FP8 gate/up: fp32 or e4m3
+    assert gg(s8, w8, 0, fm.FMOE_FP32) == fm.FMOE_ERR_ARG                          # activation scales missing
+    assert gg(s8, w8, 0, fm.FMOE_FP8_E4M3, a_scale=P(0x500)) == fm.FMOE_ERR_ARG   # code scales missing
+    assert gg(s8, w, 0, fm.FMOE_FP32, a_scale=P(0x500)) == fm.FMOE_ERR_ARG        # FP8 needs weight scales
+    s0 = fm.make_shape(0, 256, 128, 8, 2)
+    assert lib.fmoe_grouped_gemm(ctypes.byref(s0), None, 0, None, None, None, ctypes.byref(w), fm.FMOE_BF16, None,
+                                 None, None, 0, None) == fm.FMOE_OK
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_workspace_layout_buffers_fit_and_do_not_overlap(fp8):
+    T, H, I, E, k = 300, 2048, 768, 128, 8
+    s = fm.make_shape(T, H, I, E, k, fp8=fp8)
+    lay = fm.fmoe_workspace_layout(s)
+    n = T * k
+    sizes = dict(x_codes=T * H, x_scales=T * (H // 128) * 4, h_f32=n * I * 4, h_codes=n * I,
+                 h_scales=n * (I // 128) * 4, h_bf16=n * I * 2, y=n * H * 2, perm_src=n * 4, inv_perm=n * 4)
+    assert lay["total"] == fm.fmoe_workspace_bytes(s)
+    present = {k_: v for k_, v in lay.items() if k_ != "total" and v}
+    expect = {"x_codes", "x_scales", "h_f32", "h_codes", "h_scales"} if fp8 else {"h_bf16"}
+    assert set(present) == expect | {"y", "perm_src", "inv_perm"}
+    spans = sorted((off, off + sizes[name], name) for name, off in present.items())
+    for (a0, a1, na), (b0, b1, nb) in zip(spans, spans[1:]):
+        assert a1 <= b0, f"{na} overlaps {nb}"
+    assert spans[-1][1] <= lay["total"] and all(off % 256 == 0 for off in present.values())
