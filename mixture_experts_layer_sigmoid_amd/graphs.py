@@ -6,11 +6,12 @@ bucket >= T), static buffers of B rows and one HIP graph of an fmoe_forward call
 call copies the T real rows of x and of the router logits in, sets rows T..B-1 of both to NaN,
 replays the graph and returns views of the first T rows of the static outputs.
 
-NaN padding rows are the data-parallel padding case of "[Bug]: illegal memory access in
-moe_align_block_size with DP padding" (the issue's reproduction pads with NaN logits): the
-router replaces NaN by -FLT_MAX and still picks k distinct experts (the lowest indices), so the
-padding rows cost some work in experts 0..k-1, and every kernel treats rows independently (the
-FP8 activation quantizer gives every row its own scales), so they cannot change a real row.
+NaN padding rows are the case of "PR #39593: [Bug]: Fix FlashInfer CUTLASS BF16 + CUDA graphs
+IMA", Root cause: under CUDA graphs with data parallelism every rank pads its batch to one size,
+and the padding rows carry NaN into the router.  The router replaces NaN by -FLT_MAX and still
+picks k distinct experts (the lowest indices), so the padding rows cost some work in experts
+0..k-1, and every kernel treats rows independently (the FP8 activation quantizer gives every
+row its own scales), so they cannot change a real row.
 
 Everything here is plumbing around the library's entry point: torch copies and fills of the
 static buffers, and torch.cuda.CUDAGraph capture and replay.  Every step of the layer runs in

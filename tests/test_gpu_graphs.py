@@ -23,9 +23,6 @@ def check_real_rows(L, out, ids, wts):
     assert row_rel_err(got, ref) <= (FP8_TOL if L.fp8 else BF16_TOL)
 
 
-@pytest.mark.skip(reason="its one GPU run ended in a host segmentation fault inside torch's first CUDA "
-                         "initialisation (the first .cuda() of the process, before any library call); the "
-                         "cause is not shown, so the case stays off the GPU")
 @pytest.mark.parametrize("fp8", [False, True])
 def test_bucketed_graphs_with_nan_padding_rows(fp8):
     H, I, E, k = 512, 256, 16, 4

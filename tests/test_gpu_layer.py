@@ -1,5 +1,6 @@
 """GPU parity of the whole layer against the oracle: routing bit-exact, outputs within
-2e-2 (bf16) / 6e-2 (FP8) max row relative error; full sizes on token samples; edge cases."""
+2e-2 (bf16) / 6e-2 (FP8) max row relative error; every token at the full workload sizes (so every
+row tile and every 16-row block of a heavy tile is checked); edge cases."""
 import numpy as np
 import pytest
 import torch
@@ -8,6 +9,8 @@ import mixture_experts_layer_sigmoid_amd as fm
 import oracle
 from mixture_experts_layer_sigmoid_amd import synth
 from gpu_common import BF16_TOL, FP8_TOL, Layer, announce, check_layer, row_rel_err, sample_tokens
+
+ALL = 10 ** 9  # every token of the batch against the oracle (all row tiles and 16-row blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,7 +93,7 @@ def test_layer_multi_light_tiles(fp8, routing):
 def test_bf16_layer_2048x768_e128_top8_uniform(T):
     announce(f"bf16 H=2048 I=768 E=128 k=8 uniform T={T}")
     L = Layer(config=synth.BF16_LAYER, T=T, H=2048, I=768, E=128, k=8)
-    r = check_layer(L, n_sample=24)
+    r = check_layer(L, n_sample=ALL)
     print(f"T={T} max row rel err {r['err']:.3e}")
 
 
@@ -98,7 +101,7 @@ def test_bf16_layer_2048x768_e128_top8_uniform(T):
 def test_bf16_layer_2048x768_e128_top8_concentrated(T):
     announce(f"bf16 H=2048 I=768 E=128 k=8 concentrated T={T}")
     L = Layer(config=synth.BF16_LAYER, T=T, H=2048, I=768, E=128, k=8, routing="concentrated")
-    check_layer(L, n_sample=24)
+    check_layer(L, n_sample=ALL)
 
 
 @pytest.mark.parametrize("T", [128, 256])
@@ -107,7 +110,7 @@ def test_fp8_layer_2048x768_e128_top8_concentrated(T):
     announce(f"fp8 H=2048 I=768 E=128 k=8 concentrated T={T}")
     L = Layer(config=synth.FP8_LAYER, weight_config=synth.BF16_LAYER, T=T, H=2048, I=768, E=128, k=8, fp8=True,
               routing="concentrated")
-    check_layer(L, n_sample=24)
+    check_layer(L, n_sample=ALL)
     ws = fm.workspace(L.shape)
     L.forward(ws)
     st = fm.fmoe_read_stats(ws)
@@ -118,7 +121,7 @@ def test_fp8_layer_2048x768_e128_top8_concentrated(T):
 def test_fp8_layer_2048x768_e128_top8(T):
     announce(f"fp8 H=2048 I=768 E=128 k=8 T={T}")
     L8 = Layer(config=synth.FP8_LAYER, weight_config=synth.BF16_LAYER, T=T, H=2048, I=768, E=128, k=8, fp8=True)
-    check_layer(L8, n_sample=24)
+    check_layer(L8, n_sample=ALL)
     # beside the bf16 layer the weights were quantised from (information; loose bound)
     Lb = Layer(config=synth.FP8_LAYER, weight_config=synth.BF16_LAYER, T=T, H=2048, I=768, E=128, k=8)
     o8 = L8.forward()[0].float().cpu().numpy()
@@ -133,7 +136,7 @@ def test_fp8_local_shard_288_tokens_top6_of_400(routing):
     announce(f"fp8 H=7168 I=2048 E=400 (ep 8, rank 0) k=6 T=288 {routing}")
     L = Layer(config=synth.EP_SHARD, T=288, H=7168, I=2048, E=400, k=6, ep_size=8, ep_rank=0, fp8=True,
               routing=routing)
-    check_layer(L, n_sample=12)
+    check_layer(L, n_sample=ALL)
 
 
 def test_experts_all_tokens_one_expert_duplicates_and_dropped_ids():
@@ -405,3 +408,24 @@ def test_small_batch_fused_router_and_grouping(T, H, I, E, k, ep, fp8, scoring, 
     assert fm.fmoe_read_stats(ws) == st_fwd
     assert torch.equal(out_e, out)
     check_layer(L, n_sample=10 ** 6)
+
+
+# Heavy row tiles of every staged size checked on every token: caller ids give experts of
+# 17..513 rows (one to three heavy tiles of 1..4 staged 64-row groups), ragged and empty experts.
+@pytest.mark.parametrize("fp8", [False, True])
+def test_heavy_tiles_of_every_size_on_every_token(fp8):
+    announce(f"heavy tiles of 17..513 rows on every token, fp8={fp8}")
+    counts = [0, 1, 15, 16, 17, 31, 32, 33, 64, 65, 128, 129, 256, 257, 300, 513]
+    T, H, I, E, k = 470, 512, 384, 16, 4
+    flat = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    pad = np.full(T * k - len(flat), -1, np.int32)
+    ids = np.random.default_rng(7).permutation(np.concatenate([flat, pad])).reshape(T, k)
+    L = Layer(config=112, T=T, H=H, I=I, E=E, k=k, fp8=fp8)
+    wts = np.random.default_rng(8).random((T, k)).astype(np.float32)
+    ws = fm.workspace(L.shape)
+    out = fm.fmoe_experts(L.shape, L.x_gpu, torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda(), L.w, ws=ws)
+    st = fm.fmoe_read_stats(ws)
+    assert st["local_rows"] == sum(counts) and st["heavy_tiles"] >= 12
+    ref = L.oracle_tokens(ids, wts.astype(np.float64), np.arange(T, dtype=np.int32))
+    err = row_rel_err(out.float().cpu().numpy(), ref)
+    assert err <= (FP8_TOL if fp8 else BF16_TOL), f"{err:.3e}"
