@@ -195,6 +195,19 @@ def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None, 
     wall = (time.perf_counter() - t0) / steps
     pair_us = [ev[i][pair[0]].elapsed_time(ev[i][pair[1]]) * 1e3 for i in range(steps) if ev[i] is not None]
 
+    # warm secondary figure: the same weight copy and batch every call (weights stay in the
+    # caches between calls), timed back to back between one event pair
+    wa, wb = HipEvent(), HipEvent()
+    for i in range(3):
+        call(0)
+    wa.record()
+    for i in range(steps):
+        x, lg = batches[0]
+        fm.fmoe_forward(shape, x, lg, copies[0], ws=ws, out=out)
+    wb.record()
+    torch.cuda.synchronize()
+    warm_us = wa.elapsed_time(wb) * 1e3 / steps
+
     # stage breakdown: a separate pass with every event (each record adds about a microsecond)
     full = [[HipEvent() for _ in range(NS + 1)] for _ in range(steps)]
     for i in range(steps):
@@ -210,6 +223,7 @@ def measure(wl: Workload, steps: int, warmup: int, dominant: str | None = None, 
     del copies, batches, ws, out
     torch.cuda.empty_cache()
     return dict(wall_s=wall, pair_us=pair_us, dominant=dominant, stage_us=stage_us, touched=touched, rows=rows,
+                warm_us=warm_us,
                 max_rows=max_rows, rows_estimate=used[0]["rows_estimate"], tile_rows=used[0]["tile_rows"],
                 copies=n_copies)
 
@@ -221,6 +235,7 @@ def summarize(wl: Workload, m: dict) -> dict:
     flops = 6.0 * m["rows"] * wl.H * wl.I
     return dict(**wl.describe(), us_p20=round(pct(call_us, 20), 2), us_p50=round(p50, 2),
                 us_p80=round(pct(call_us, 80), 2), us_wall=round(m["wall_s"] * 1e6, 2),
+                us_warm=round(m["warm_us"], 2),
                 touched_experts=round(m["touched"], 2), touched_MB=round(tb / 1e6, 1),
                 hbm_TBps=round(tb / (p50 * 1e-6) / 1e12, 3), tokens_per_s=round(wl.T / (p50 * 1e-6), 1),
                 mfma_util=round(flops / (p50 * 1e-6) / (MFMA_PEAK_TFLOPS[wl.dtype] * 1e12), 4),
@@ -300,12 +315,16 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload_name: str, st
     return ent
 
 
-def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
-    """The CPU oracle (as it stands) on a bounded token sample of batch 0 of the workload."""
+def cpu_baseline(wl: Workload, target_s: float = 12.0, threads: int = 0) -> dict:
+    """The CPU oracle (as it stands) on a bounded token sample of batch 0 of the workload, on
+    `threads` OpenMP threads (0: all of them)."""
     import numpy as np
 
     import oracle
     from mixture_experts_layer_sigmoid_amd import synth
+
+    all_threads = oracle.num_threads()  # OpenMP's default: OMP_NUM_THREADS, else every core
+    oracle.set_num_threads(threads if threads > 0 else all_threads)
 
     x = synth.activations(wl.config, wl.T, wl.H, seed=0)
     lg = synth.routed_logits(wl.config, wl.T, wl.E, wl.k, wl.routing, seed=0)
@@ -315,7 +334,7 @@ def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
     wg, wu, wd = (synth.bf16_bits(t) for t in synth.expert_weights_bf16(wl.weight_config, wl.El, wl.H, wl.I))
     xb = synth.bf16_bits(x)
     threads = oracle.num_threads()
-    done, spent, n = 0, 0.0, max(threads, 8)
+    done, spent, n = 0, 0.0, max(threads, 1)
     while spent < target_s and done < wl.T:
         tok = np.arange(done, min(wl.T, done + n), dtype=np.int32)
         t0 = time.perf_counter()
@@ -324,6 +343,7 @@ def cpu_baseline(wl: Workload, target_s: float = 12.0) -> dict:
         done += len(tok)
         n *= 2
     per_call = spent / done * wl.T + route_s
+    oracle.set_num_threads(all_threads)
     touched = len(np.unique(ids)) * wl.expert_bytes()
     return dict(value=round(touched / per_call / 1e12, 6), unit="TB/s", cores=threads, kind="oracle",
                 us_per_call=round(per_call * 1e6, 1),
@@ -381,6 +401,60 @@ def cpu_oracle_sample(wl: Workload, cache: dict) -> dict:
     return dict(cpu_oracle_us=round(per_call * 1e6, 1),
                 cpu_sample=f"{n} of {wl.T} tokens of batch 0 ({len(local)} local experts, {spent:.2f} s), router on "
                            f"all tokens, {threads} threads")
+
+
+def router_microbench(samples: int = 24, warmup: int = 5, batch_calls: int = 200) -> dict:
+    """The router alone on the pages' micro-benchmark batch: 128 tokens x 128 experts bf16 logits,
+    top-8, 10% NaN plus 4 all-NaN rows, softmax and sigmoid (renormalised).  Per call: an event
+    pair around one call, with a device fill enqueued before the pair so the GPU is still busy
+    while the host enqueues (the interval is device time only); p20/p50/p80 over `samples` calls
+    after `warmup`.  Also the mean over `batch_calls` calls back to back."""
+    import ctypes
+
+    import torch
+
+    import mixture_experts_layer_sigmoid_amd as fm
+    from mixture_experts_layer_sigmoid_amd import synth
+
+    lib = fm.load_library()
+    T, E, k = 128, 128, 8
+    lg = synth.router_batch(T, E, k).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    busy = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, sc in (("softmax", fm.FMOE_SOFTMAX), ("sigmoid", fm.FMOE_SIGMOID)):
+        def call():
+            rc = lib.fmoe_router_topk(ctypes.c_void_p(lg.data_ptr()), fm.FMOE_BF16, T, E, k, sc, 1,
+                                      ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(wts.data_ptr()), st)
+            if rc != fm.FMOE_OK:
+                raise RuntimeError(f"fmoe_router_topk: status {rc}")
+        for _ in range(warmup):
+            call()
+        us = []
+        for _ in range(samples):
+            a, b = HipEvent(), HipEvent()
+            busy.fill_(1.0)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            us.append(a.elapsed_time(b) * 1e3)
+        a, b = HipEvent(), HipEvent()
+        busy.fill_(1.0)
+        a.record()
+        for _ in range(batch_calls):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = dict(us_p20=round(pct(us, 20), 2), us_p50=round(pct(us, 50), 2), us_p80=round(pct(us, 80), 2),
+                         us_back_to_back=round(a.elapsed_time(b) * 1e3 / batch_calls, 2))
+    del busy
+    return dict(workload="router only: 128 tokens x 128 experts bf16, top-8, 10% NaN + 4 all-NaN rows, renormalised",
+                samples=samples, warmup=warmup, **res,
+                pages_context="topk_softmax p50 10.24 us, topk_sigmoid p50 12.16 us with the NaN check fused, on B200 "
+                              "(another GPU and another kernel: context only)")
 
 
 def tile_sweep(workloads, steps: int = 10) -> list:
@@ -561,10 +635,16 @@ def main():
             sweep.append(summarize(wl, measure(wl, args.sweep_steps, 3)))
             print(f"[bench]   p50 {sweep[-1]['us_p50']} us, {sweep[-1]['hbm_TBps']} TB/s", file=sys.stderr, flush=True)
 
+    print("[bench] router micro-benchmark (128 x 128, top-8, 10% NaN)", file=sys.stderr, flush=True)
+    router = router_microbench()
+
     cpu = None
     if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        print("[bench] cpu baseline (oracle, all cores)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(head)
+        print("[bench] cpu baseline (oracle, 1 core)", file=sys.stderr, flush=True)
+        one = cpu_baseline(head, threads=1)
+        cpu["one_core"] = dict(value=one["value"], us_per_call=one["us_per_call"], cores=1, sample=one["sample"])
         hs.update(cpu_oracle_us=cpu["us_per_call"], cpu_sample=cpu["sample"])
         if not args.no_sweep:
             cache = {}
@@ -581,9 +661,11 @@ def main():
                 dtype="bf16", data="synthetic",
                 config=dict(**head.describe(), us_per_call=round(m["wall_s"] * 1e6, 2),
                             tokens_per_s=round(head.T / m["wall_s"], 1),
+                            warm_us_per_call=round(m["warm_us"], 2),
                             mfma_util=round(6.0 * m["rows"] * head.H * head.I / m["wall_s"] / 2.5e15, 4),
                             weight_copies=m["copies"]),
-                roofline=roof, cpu_baseline=cpu, host_cpu=host_cpu(), kernel_sha=kernel_hash(),
+                roofline=roof, cpu_baseline=cpu, router_microbench=router, host_cpu=host_cpu(),
+                host_cores=os.cpu_count(), kernel_sha=kernel_hash(),
                 sweep=sweep)
     print(json.dumps(line))
 
