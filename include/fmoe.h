@@ -273,6 +273,27 @@ int fmoe_forward_profiled(const fmoe_shape* shape, const void* x, const void* lo
                           float* topk_weights_out, void* ws, size_t ws_bytes, void* stream,
                           void* const* stage_events);
 
+/* Largest workspace fmoe_forward_noalloc can use: the size of the library's static device
+ * buffer (one per GPU the library runs on, held until the process ends). */
+#define FMOE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+
+/* fmoe_forward without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static device buffer of FMOE_NOALLOC_MAX_WORKSPACE bytes inside the library,
+ * one per GPU; the first call on a GPU looks up that GPU's copy (hipGetSymbolAddress, which
+ * allocates nothing) and keeps its address.  The call itself allocates nothing and calls no
+ * allocating routine.  A shape whose fmoe_workspace_bytes exceeds the buffer returns
+ * FMOE_ERR_WORKSPACE and enqueues nothing (the 2048/768/128-expert top-8 layer fits up to
+ * T = 1024 in bf16; the 7168-wide FP8 shard at T = 288 fits).  Every call on one GPU shares
+ * that GPU's buffer, which keeps the last call's contents; nothing in it needs to start at
+ * zero (each call writes every value it later reads).  Calls that overlap on one GPU (two
+ * streams or two threads) race on the buffer: the caller must order them.  Works on the
+ * current device; the stream must belong to it.  Arguments and results otherwise as
+ * fmoe_forward; fmoe_read_stats cannot read this buffer. */
+int fmoe_forward_noalloc(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype,
+                         int32_t scoring, int32_t renormalize, const fmoe_weights* w, void* out,
+                         int32_t* topk_ids_out, float* topk_weights_out, void* stream);
+
 /* Copies the counters of the last call that used ws into *out.  Synchronises the stream:
  * for tests and benchmarks, not for the hot path. */
 int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out);

@@ -24,7 +24,7 @@ STAGES = ("router", "group", "quant_x", "gemm1", "gemm1_heavy", "quant_h", "gemm
 EXPORTED = ("fmoe_abi_version", "fmoe_status_string", "fmoe_workspace_bytes", "fmoe_router_logits",
             "fmoe_router_topk", "fmoe_route_permute", "fmoe_experts", "fmoe_forward", "fmoe_forward_profiled",
             "fmoe_forward_planned", "fmoe_router_topk_grouped", "fmoe_read_stats", "fmoe_act_quant",
-            "fmoe_workspace_layout", "fmoe_grouped_gemm")
+            "fmoe_workspace_layout", "fmoe_grouped_gemm", "fmoe_forward_noalloc")
 
 
 class fmoe_shape(ctypes.Structure):
@@ -87,6 +87,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fmoe_forward_planned.argtypes = lib.fmoe_forward.argtypes + [ctypes.POINTER(fmoe_plan)]
     lib.fmoe_read_stats.argtypes = [P, P, ctypes.POINTER(fmoe_stats)]
     lib.fmoe_act_quant.argtypes = [P, i32, ctypes.c_int64, i32, P, P, P]
+    lib.fmoe_forward_noalloc.argtypes = [ctypes.POINTER(fmoe_shape), P, P, i32, i32, i32,
+                                         ctypes.POINTER(fmoe_weights), P, P, P, P]
     lib.fmoe_workspace_layout.argtypes = [ctypes.POINTER(fmoe_shape), ctypes.POINTER(fmoe_layout)]
     lib.fmoe_grouped_gemm.argtypes = [ctypes.POINTER(fmoe_shape), ctypes.POINTER(fmoe_plan), i32, P, P, P,
                                       ctypes.POINTER(fmoe_weights), i32, P, P, P, sz, P]
@@ -368,3 +370,29 @@ def fmoe_grouped_gemm(shape: fmoe_shape, stage: int, topk_ids: torch.Tensor, a: 
                                             _ptr(topk_ids), _ptr(a), _ptr(a_scale), ctypes.byref(ws_struct), out_dtype,
                                             _ptr(out), _ptr(out_scale), _ptr(ws), ws.numel(), _stream(dev)))
     return (out, out_scale) if out_dtype == FMOE_FP8_E4M3 else out
+
+
+NOALLOC_MAX_WORKSPACE = 64 << 20  # FMOE_NOALLOC_MAX_WORKSPACE
+
+
+def fmoe_forward_noalloc(shape: fmoe_shape, x: torch.Tensor, logits: torch.Tensor, w: ExpertWeights,
+                         scoring: int = FMOE_SOFTMAX, renormalize: bool = True, out: torch.Tensor | None = None,
+                         routing_out: tuple | None = None):
+    """fmoe_forward on the library's static per-GPU workspace (no workspace argument; the C call
+    allocates nothing).  out and routing_out may be preallocated; returns out, or (out, ids,
+    weights) when routing_out is given."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(logits, "logits")
+    dev = x.device
+    out = torch.empty((shape.tokens, shape.hidden), dtype=torch.bfloat16, device=dev) if out is None else out
+    ids = wts = None
+    if routing_out is not None:
+        ids, wts = routing_out
+        _dev(ids, "routing ids", torch.int32)
+        _dev(wts, "routing weights", torch.float32)
+    ws_struct = w.struct()
+    _check("fmoe_forward_noalloc",
+           load_library().fmoe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(logits), _dtype_code(logits),
+                                               scoring, int(bool(renormalize)), ctypes.byref(ws_struct), _ptr(out),
+                                               _ptr(ids), _ptr(wts), _stream(dev)))
+    return out if routing_out is None else (out, ids, wts)

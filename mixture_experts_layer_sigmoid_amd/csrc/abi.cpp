@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fmoe.h"
 #include "launch.hpp"
@@ -444,6 +445,35 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
 
 }  // namespace
 
+// Workspace of fmoe_forward_noalloc: a static device buffer, one copy per GPU (the code object
+// is loaded on every device the library runs on).  Host code never passes this name to a
+// kernel or a copy: the name is a host-side stand-in, and only the device address that
+// hipGetSymbolAddress returns for the current device is used.
+static __device__ __align__(256) unsigned char scratch[FMOE_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device.
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FMOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FMOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FMOE_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FMOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fmoe_abi_version(void) { return FMOE_ABI_VERSION; }
@@ -622,6 +652,18 @@ int fmoe_grouped_gemm(const fmoe_shape* shape, const fmoe_plan* plan, int32_t st
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
     log_plan(stage == 0 ? "fmoe_grouped_gemm gate/up" : "fmoe_grouped_gemm down", p);
     return run_stage(p, stage, topk_ids, a, a_scale, w, mode, out, out_scale, (char*)ws, (hipStream_t)stream);
+}
+
+int fmoe_forward_noalloc(const fmoe_shape* shape, const void* x, const void* logits, int32_t logits_dtype,
+                         int32_t scoring, int32_t renormalize, const fmoe_weights* w, void* out,
+                         int32_t* topk_ids_out, float* topk_weights_out, void* stream) {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (make_plan(shape).L.total > FMOE_NOALLOC_MAX_WORKSPACE) return FMOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (shape->tokens > 0 && (rc = scratch_of_current_device(&ws))) return rc;
+    return forward_impl(shape, x, logits, logits_dtype, scoring, renormalize, w, out, topk_ids_out, topk_weights_out,
+                        ws, FMOE_NOALLOC_MAX_WORKSPACE, stream, nullptr);
 }
 
 int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {
