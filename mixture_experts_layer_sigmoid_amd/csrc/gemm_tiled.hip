@@ -52,9 +52,13 @@ __device__ __forceinline__ void tg_wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void tg_fence() { asm volatile("" ::: "memory"); }
-// workgroup barrier without the full memory wait __syncthreads implies around LDS DMA
+// Workgroup barrier without the full memory wait __syncthreads implies around LDS DMA.  The
+// wavefront's own LDS reads finish first: after the barrier other wavefronts copy the next
+// stage into the buffer those reads came from, and the scheduler may otherwise sink the
+// reads' wait (with the MFMAs that use them) below the barrier.
 __device__ __forceinline__ void tg_barrier() {
     tg_fence();
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
     __builtin_amdgcn_s_barrier();
     tg_fence();
 }
