@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define FMOE_ABI_VERSION 3
+#define FMOE_ABI_VERSION 4
 
 /* Limits of the library (checked, FMOE_ERR_UNSUPPORTED beyond them). */
 #define FMOE_MAX_EXPERTS 1024     /* experts (total) for the router; local experts likewise   */
@@ -95,6 +95,11 @@ typedef struct {
     int32_t heavy_tiles;     /* row tiles of the experts cut into heavy tiles               */
     int32_t heavy_rows;      /* host plan: rows of a full heavy tile (an expert with c rows
                                 gets ceil(c / heavy_rows) tiles of about equal size)         */
+    int32_t light_rows;      /* rows of the light tiles                                     */
+    int32_t split_light_tiles; /* light tiles whose gate/up GEMM ran on the split-reduction
+                                kernel because they held few rows on average (the grouping's
+                                choice from the real counts; 0: the streaming kernel or the
+                                host plan's kernel took them)                                  */
 } fmoe_stats;
 
 int fmoe_abi_version(void);

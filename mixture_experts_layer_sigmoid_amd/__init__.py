@@ -56,7 +56,8 @@ class fmoe_stats(ctypes.Structure):
     _fields_ = [("dropped_ids", ctypes.c_int64), ("local_rows", ctypes.c_int32), ("max_rows", ctypes.c_int32),
                 ("empty_experts", ctypes.c_int32), ("m_tiles", ctypes.c_int32), ("rows_estimate", ctypes.c_int32),
                 ("tile_rows", ctypes.c_int32), ("heavy_tiles", ctypes.c_int32),
-                ("heavy_rows", ctypes.c_int32)]
+                ("heavy_rows", ctypes.c_int32), ("light_rows", ctypes.c_int32),
+                ("split_light_tiles", ctypes.c_int32)]
 
 
 _lib = None

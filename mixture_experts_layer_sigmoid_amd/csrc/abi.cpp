@@ -51,6 +51,8 @@ struct Plan {
     int max_light;       // bounds on light and heavy row tiles for any routing
     int max_heavy;
     int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
+    int sparse_rows;     // > 0: the forward also launches the split gate/up kernel (split 2) for
+                         // light tiles of fewer rows than this on average (decided on the device)
     Layout L;
 };
 
@@ -131,6 +133,16 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr, long long max
     };
     p.wk1 = ov && ov->split_gate_up ? ov->split_gate_up : pick_wk(p.I, true);
     p.wk2 = ov && ov->split_down ? ov->split_down : pick_wk(p.H, false);
+    // Routing concentration, read on the device ([H20] paragraph 4): where the heuristic streams
+    // the bf16 gate/up GEMM unsplit (16 to 31 expected rows per expert), the grouping hands the
+    // light tiles to the split-reduction kernel instead when they hold fewer than a quarter of the
+    // expected rows on average.  Those are the cold experts of a concentrated batch (one or two
+    // rows each, their hot experts in heavy tiles); the tile-space sweep measured them faster
+    // split in two (T=256 concentrated: 250.5 against 260.8 us) and uniform routing, whose light
+    // tiles hold about the expected rows, faster streamed (254.3 against 290.1 us).  The launch
+    // of the kernel left without tiles costs about a microsecond and a half.
+    p.sparse_rows = (!p.fp8 && p.wk1 == 1 && !(ov && ov->split_gate_up) && p.rows_estimate >= 8)
+                        ? p.rows_estimate / 4 : 0;
     // FP8: several light tiles per expert (up to kMaxLightPerExpert) when that bounds every
     // expert.  The heavy-tile launches are then left out, and the gate/up kernel writes the
     // quantised activation itself (no quantisation launch, no fp32 activation); the light tiles
@@ -215,9 +227,10 @@ void log_plan(const char* who, const Plan& p) {
     std::fprintf(stderr,
                  "[fmoe] %s: T=%d H=%d I=%d E=%d k=%d E_loc=%d first_expert=%d %s | rows_estimate=%d "
                  "tile_rows=%d light_cap=%d heavy_launch=%d heavy_rows=%d split_gate_up=%d split_down=%d "
-                 "max_light_tiles=%d max_heavy_tiles=%d workspace=%zu B\n",
+                 "sparse_rows=%d max_light_tiles=%d max_heavy_tiles=%d workspace=%zu B\n",
                  who, p.T, p.H, p.I, p.E, p.k, p.El, p.lo, p.fp8 ? "fp8" : "bf16", p.rows_estimate, p.tile_rows,
-                 p.light_cap, (int)p.heavy_launch, p.heavy_rows, p.wk1, p.wk2, p.max_light, p.max_heavy, p.L.total);
+                 p.light_cap, (int)p.heavy_launch, p.heavy_rows, p.wk1, p.wk2, p.sparse_rows, p.max_light, p.max_heavy,
+                 p.L.total);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FMOE_OK : FMOE_ERR_HIP; }
@@ -257,7 +270,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     MTile* mtiles_heavy = mtiles + p.max_light;
     if (!grouped)
         FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate,
-                          (int32_t*)(ws + L.counts),
+                              p.sparse_rows, (int32_t*)(ws + L.counts),
                           (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
                           mtiles_heavy, hdr, st));
     const bool heavy_possible = p.heavy_launch;
@@ -288,10 +301,18 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     GemmArgs g1h = g1;
     g1h.mtiles = mtiles_heavy;
     g1h.tile_count = &hdr->m_tiles_heavy;
-    if (p.wk1 == 1)
+    if (p.wk1 == 1) {
+        GemmArgs g1s = g1;  // the light tiles' other kernel (the grouping gives all of them to one)
+        if (p.sparse_rows > 0) {
+            g1.tile_count = &hdr->m_tiles_stream;
+            g1s.tile_count = &hdr->m_tiles_split;
+        }
         FMOE_TRY(launch_grouped_gemm_stream(true, p.fp8, fused_quant_h ? kOutE4M3 : p.fp8 ? kOutF32 : kOutBf16, g1,
                                             p.tile_rows, p.max_light, cus, st));
-    else FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_light, cus, st));
+        if (p.sparse_rows > 0) FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1s, p.tile_rows, 2, p.max_light, cus, st));
+    } else {
+        FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_light, cus, st));
+    }
     record(ev, FMOE_STAGE_GEMM1_HEAVY, st);
     if (heavy_possible) FMOE_TRY(launch_grouped_gemm_tiled(true, p.fp8, p.fp8, g1h, p.max_heavy, cus, st));
 
@@ -342,7 +363,7 @@ int run_stage(const Plan& p, int stage, const int32_t* ids, const void* a, const
     MTile* mtiles = (MTile*)(ws + L.mtiles);
     MTile* mtiles_heavy = mtiles + p.max_light;
     const int cus = device_cus();
-    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate,
+    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate, 0,
                           (int32_t*)(ws + L.counts), (int32_t*)(ws + L.offsets), perm, (int32_t*)(ws + L.inv),
                           (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles, mtiles_heavy, hdr, st));
     GemmArgs g;
@@ -434,7 +455,8 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
         const Layout& L = p.L;
         MTile* mtiles = (MTile*)(wsb + L.mtiles);
         FMOE_TRY(launch_route_group(logits, bf16, (int)p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, p.El, p.lo,
-                                    p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate, (int32_t*)(wsb + L.counts),
+                                    p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate, p.sparse_rows,
+                                    (int32_t*)(wsb + L.counts),
                                     (int32_t*)(wsb + L.offsets), (int32_t*)(wsb + L.perm), (int32_t*)(wsb + L.inv),
                                     mtiles, mtiles + p.max_light, (DevHeader*)(wsb + L.hdr), st, xqp));
         return run_experts(p, x, ids, wts, w, out, wsb, st, ev, true, p.fp8);
@@ -545,8 +567,7 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
     char* wsb = (char*)ws;
     MTile* mt = (MTile*)(wsb + p.L.mtiles);
     return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows,
-                                   p.rows_estimate,
-                                   counts, offsets,
+                                   p.rows_estimate, p.sparse_rows, counts, offsets,
                                    perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp), mt,
                                    mt + p.max_light, (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));
 }
@@ -682,6 +703,8 @@ int fmoe_read_stats(const void* ws, void* stream, fmoe_stats* out) {
     out->heavy_rows = h.heavy_rows;
     out->tile_rows = h.tile_rows;
     out->rows_estimate = h.rows_estimate;
+    out->light_rows = h.light_rows;
+    out->split_light_tiles = h.m_tiles_split;
     return FMOE_OK;
 }
 

@@ -30,7 +30,10 @@ struct DevHeader {
     int32_t rows_estimate;  // max(1, ceil(T*top_k/E)) of the host plan
     int32_t m_tiles_heavy;  // heavy row tiles (experts with more than the light limit)
     int32_t heavy_rows;     // rows of a full heavy tile
-    int32_t pad[6];
+    int32_t light_rows;     // rows of the light tiles
+    int32_t m_tiles_stream; // light tiles of the streaming gate/up kernel (all or none of them)
+    int32_t m_tiles_split;  // light tiles of the split-reduction gate/up kernel (the others)
+    int32_t pad[3];
 };
 static_assert(sizeof(DevHeader) == 64, "header size");
 

@@ -132,13 +132,24 @@ __device__ void block_scan4_max(const int (&v)[4], int mv, int* sh, int (&excl)[
     __syncthreads();
 }
 
+// Which gate/up kernel takes the light tiles: the split-reduction one when sparse_rows > 0 and
+// the light tiles hold fewer than sparse_rows rows on average (the cold experts of a
+// concentrated batch, one or two rows each), else the streaming one.  Decided here from the real
+// counts, so the host launches both and the one without tiles exits at once.
+__device__ __forceinline__ void write_light_split(DevHeader* hdr, int n_light, int light_rows, int sparse_rows) {
+    const bool split = sparse_rows > 0 && n_light > 0 && (long long)light_rows < (long long)sparse_rows * n_light;
+    hdr->light_rows = light_rows;
+    hdr->m_tiles_stream = split ? 0 : n_light;
+    hdr->m_tiles_split = split ? n_light : 0;
+}
+
 // Phase 2 by one workgroup of kScanThreads: turns cnt[c * El + e] (count of expert e in
 // chunk c) into the first grouped row of (e, c); writes counts, offsets, the row tiles and
 // the header.  Thread t works on expert e = t % El' and part p = t / El' of its chunks
 // (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
 // threads read consecutive experts of a chunk.
 __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int light_cap, int heavy_rows,
-                              int rows_estimate, long long dropped,
+                              int rows_estimate, int sparse_rows, long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
                               int* sh /* >= kScanShared ints */) {
@@ -162,7 +173,10 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
         for (; c < c1; c++) s += cnt[c * El + e];
     }
     int* part_sum = sh + kScanLds;  // [kScanThreads], later 3 x [512]
+    static_assert(kScanLds + 3 * 512 <= kScanShared - 1, "light-row sum clear of the part sums");
+    int* light_rows = sh + kScanShared - 1;  // rows of the light tiles (LDS atomic sum)
     part_sum[threadIdx.x] = s;
+    if (threadIdx.x == 0) *light_rows = 0;
     __syncthreads();
     int before = 0, total = 0;  // this part's prefix inside its expert, and the expert total
     for (int q = 0; q < P; q++) {
@@ -180,6 +194,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
     const int nheavy0 = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
     const int hrows = heavy ? min(heavy_rows, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
     const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0
+    if (lead && !heavy && total > 0) atomicAdd(light_rows, total);  // read after the scan's barriers
     int R, n_light, n_heavy, empty;
     // grouped rows, light tiles, heavy tiles and empty experts before each expert (valid in
     // its lead thread), their totals, and the largest expert
@@ -265,6 +280,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
         hdr->tile_rows = tile_rows;
         hdr->heavy_rows = heavy_rows;
         hdr->rows_estimate = rows_estimate;
+        write_light_split(hdr, n_light, *light_rows, sparse_rows);
     }
 }
 
@@ -286,7 +302,7 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 // All three phases by one workgroup of kScanThreads.  ids may point to global memory or to
 // LDS (generic addressing); lds holds small_lds_ints(n, El) ints.
 __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, int El, int lo, int tile_rows,
-                                            int light_cap, int heavy_rows, int rows_estimate, int32_t* __restrict__ counts,
+                                            int light_cap, int heavy_rows, int rows_estimate, int sparse_rows, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                             int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                             MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr, int* lds) {
@@ -320,7 +336,7 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
     __syncthreads();
     long long dropped = 0;
     for (int c = 0; c < nchunk; c++) dropped += bads[c];
-    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles,
+    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
                   mtiles_heavy, hdr, sh);
     __syncthreads();
 #pragma unroll
@@ -338,14 +354,14 @@ static size_t small_lds_ints(int n, int El) {
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
                                                              int lo, int tile_rows, int light_cap, int heavy_rows,
-                                                             int rows_estimate,
+                                                             int rows_estimate, int sparse_rows,
                                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
                                                              int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                                              MTile* __restrict__ mtiles_heavy,
                                                              DevHeader* __restrict__ hdr) {
     extern __shared__ int lds[];
-    group_small(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm,
+    group_small(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm,
                 mtiles, mtiles_heavy, hdr, lds);
 }
 
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
 // experts in ascending order give the offsets and the light tile slots, and each assignment
 // goes to its expert's offset plus its rank in the chunk.  cnt: El ints of LDS.
 __device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
-                           int rows_estimate, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                           int rows_estimate, int sparse_rows, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm,
                            MTile* __restrict__ mtiles, DevHeader* __restrict__ hdr, int* cnt) {
     const int lane = lane_id();
@@ -409,6 +425,7 @@ __device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int
         hdr->tile_rows = tile_rows;
         hdr->heavy_rows = heavy_rows;
         hdr->rows_estimate = rows_estimate;
+        write_light_split(hdr, run_tiles, run_rows, sparse_rows);
     }
 }
 
@@ -425,7 +442,7 @@ constexpr int kWaveGroupTokens = 16;
 template <int SLOTS, bool BF16_IN, bool QX>
 __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
     const void* __restrict__ logits, int T, int E, int k, int scoring, int renorm, int32_t* __restrict__ ids,
-    float* __restrict__ weights, int El, int lo, int tile_rows, int light_cap, int heavy_rows, int rows_estimate,
+    float* __restrict__ weights, int El, int lo, int tile_rows, int light_cap, int heavy_rows, int rows_estimate, int sparse_rows,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
     DevHeader* __restrict__ hdr, XQuant xq) {
@@ -442,11 +459,11 @@ __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
     __syncthreads();
     if (n <= 64 && T <= kWaveGroupTokens) {
         if (w == 0)
-            group_wave(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, counts, offsets, perm_src,
+            group_wave(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src,
                        inv_perm, mtiles, hdr, lds + ((n + 3) & ~3));
         return;
     }
-    group_small(ids_lds, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, counts, offsets, perm_src,
+    group_small(ids_lds, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src,
                 inv_perm, mtiles, mtiles_heavy, hdr, lds + ((n + 3) & ~3));
 }
 
@@ -469,7 +486,7 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int light_cap, int heavy_rows, int rows_estimate,
+                                                            int light_cap, int heavy_rows, int rows_estimate, int sparse_rows,
                                                             const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, dropped, counts, offsets, mtiles,
+    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
                   mtiles_heavy, hdr, sh);
 }
 
@@ -505,13 +522,13 @@ size_t group_scratch_bytes(long long n, int El) {
 }
 
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
-                        int heavy_rows, int rows_estimate,
+                        int heavy_rows, int rows_estimate, int sparse_rows,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
     const size_t lds = small_lds_ints(n, El) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
-        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate,
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows,
                                                     counts,
                                                     offsets,
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
@@ -520,7 +537,7 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
     int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, bad,
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, bad,
                                              counts,
                                              offsets, mtiles,
                                              mtiles_heavy, hdr);
@@ -543,7 +560,7 @@ bool route_group_fits(int T, int k, int E, int El) {
 template <int SLOTS>
 static void launch_route_group_slots(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                                      int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
-                                     int heavy_rows, int rows_estimate, int32_t* counts, int32_t* offsets,
+                                     int heavy_rows, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets,
                                      int32_t* perm_src, int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy,
                                      DevHeader* hdr, hipStream_t st, const XQuant* xq) {
     const size_t lds = route_group_lds_bytes(T, k, El);
@@ -553,13 +570,13 @@ static void launch_route_group_slots(const void* logits, bool bf16, int T, int E
     // workgroup 0 routes and groups; FP8: one more workgroup per 16 groups of x to quantise
     const unsigned blocks = xq ? 1 + (unsigned)((T * (xq->H / 128) + kScanThreads / 64 - 1) / (kScanThreads / 64)) : 1;
     kern<<<blocks, kScanThreads, lds, st>>>(logits, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows,
-                                            light_cap, heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm,
+                                            light_cap, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm,
                                             mtiles, mtiles_heavy, hdr, xq ? *xq : none);
 }
 
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
-                              int heavy_rows, int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int heavy_rows, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                               int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st,
                               const XQuant* xq) {
     if (!route_group_fits(T, k, E, El)) return hipErrorInvalidValue;
@@ -567,7 +584,7 @@ hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k
     const int slots = (E + 63) / 64;
 #define FMOE_RG(S)                                                                                                  \
     launch_route_group_slots<S>(logits, bf16, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, light_cap, \
-                                heavy_rows, rows_estimate, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy,   \
+                                heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy,   \
                                 hdr, st, xq)
     if (slots <= 1) FMOE_RG(1);
     else if (slots <= 2) FMOE_RG(2);

@@ -41,13 +41,15 @@ size_t group_scratch_bytes(long long n, int El);
 bool route_group_fits(int T, int k, int E, int El);
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
-                              int heavy_rows, int rows_estimate, int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                              int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st,
-                              const XQuant* xq = nullptr);
+                              int heavy_rows, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets,
+                              int32_t* perm_src, int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr,
+                              hipStream_t st, const XQuant* xq = nullptr);
 // light_cap >= tile_rows: experts with up to light_cap rows are cut into light tiles of tile_rows
-// rows, heavier ones into heavy tiles
+// rows, heavier ones into heavy tiles.  sparse_rows > 0: the light tiles go to the split-reduction
+// gate/up kernel (DevHeader::m_tiles_split) when they hold fewer than sparse_rows rows on
+// average, else to the streaming one (m_tiles_stream); 0: always the streaming one.
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
-                        int heavy_rows, int rows_estimate,
+                        int heavy_rows, int rows_estimate, int sparse_rows,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int cols, uint8_t* q, float* s,

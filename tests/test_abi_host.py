@@ -28,9 +28,9 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     lib = fm.load_library()
-    assert fm.fmoe_abi_version() == 3
+    assert fm.fmoe_abi_version() == 4
     text = open(HEADER).read()
-    assert "#define FMOE_ABI_VERSION 3" in text
+    assert "#define FMOE_ABI_VERSION 4" in text
     for code, word in [(0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")]:
         assert word in lib.fmoe_status_string(code)
 

@@ -104,6 +104,34 @@ def test_bf16_layer_2048x768_e128_top8_concentrated(T):
     check_layer(L, n_sample=ALL)
 
 
+@pytest.mark.parametrize("routing", ["uniform", "concentrated"])
+def test_light_gate_up_kernel_chosen_from_the_real_counts(routing):
+    # T=256 of the 128-expert bf16 layer expects 16 rows per expert.  Uniform light tiles hold
+    # about that many and stay on the streaming kernel; the cold experts of a concentrated batch
+    # hold one or two rows each and the grouping hands them to the split-reduction kernel (the
+    # hot experts are heavy tiles).  Either way the output equals, bit for bit, the forced plan
+    # that runs the same kernel on the same tiles, and the oracle on every token.
+    announce(f"bf16 T=256 {routing}: light gate/up kernel picked on the device")
+    L = Layer(config=synth.BF16_LAYER, T=256, H=2048, I=768, E=128, k=8, routing=routing)
+    ws = fm.workspace(L.shape)
+    auto = L.forward(ws)[0].clone()
+    st = fm.fmoe_read_stats(ws)
+    light = st["m_tiles"] - st["heavy_tiles"]
+    assert light > 0
+    if routing == "concentrated":
+        assert st["heavy_tiles"] > 0 and st["split_light_tiles"] == light and st["light_rows"] < 4 * light
+        forced = fm.fmoe_plan(32, 2, 1, 1)  # the split-reduction gate/up kernel (two wavefronts)
+    else:
+        assert st["split_light_tiles"] == 0 and st["light_rows"] >= 4 * light
+        forced = fm.fmoe_plan(32, 1, 1, 1)  # the streaming gate/up kernel
+    L.plan = forced
+    again = L.forward(ws)[0]
+    assert fm.fmoe_read_stats(ws)["split_light_tiles"] == 0  # a forced split leaves the choice out
+    assert torch.equal(again, auto)
+    L.plan = None
+    check_layer(L, n_sample=ALL)
+
+
 @pytest.mark.parametrize("T", [128, 256])
 def test_fp8_layer_2048x768_e128_top8_concentrated(T):
     # hot experts of ~120 / ~240 rows cut into 4 / 8 light tiles, no heavy launch
