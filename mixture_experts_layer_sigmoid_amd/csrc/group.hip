@@ -31,7 +31,8 @@ namespace fmoe {
 constexpr int kScanThreads = 1024;
 constexpr int kSmallChunks = 64;  // chunks of the one-workgroup path
 constexpr int kSmallPerWave = kSmallChunks / (kScanThreads / 64);  // chunks per wavefront there
-constexpr int kScanShared = 96 + 64 + 1536;  // LDS ints of scan_and_tile (kScanLds + part sums)
+// LDS ints of scan_and_tile for El local experts: part sums, then three per-expert arrays
+__host__ __device__ constexpr int scan_lds_ints(int El) { return kScanThreads + 3 * El; }
 
 // Phase 1 for one chunk of 64 assignments, by one wavefront.  Writes the chunk's count of
 // every local expert to col[e * col_stride] (zeros included) and returns, for this lane, the
@@ -78,60 +79,6 @@ __device__ __forceinline__ void chunk_rank(const int32_t* __restrict__ ids, int 
     chunk_rank_id(i < n ? ids[i] : 0, i < n, E, El, lo, col, col_stride, mask, out_l, out_r, bad);
 }
 
-// Exclusive sums of four values over the kScanThreads threads of the workgroup (thread
-// order), their totals, and the maximum of a fifth value, with three barriers.
-// sh: kScanLds ints of LDS.
-constexpr int kScanLds = 4 * 16 + 16 + 4 * 16 + 1;
-__device__ void block_scan4_max(const int (&v)[4], int mv, int* sh, int (&excl)[4], int (&total)[4], int* maxv) {
-    constexpr int NWV = kScanThreads / 64;
-    const int lane = lane_id(), wid = threadIdx.x >> 6;
-    int x[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) x[i] = v[i];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int y = __shfl_up(x[i], o, 64);
-            if (lane >= o) x[i] += y;
-        }
-    }
-    const int m = wave_max(mv);
-    if (lane == 63) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) sh[wid * 4 + i] = x[i];
-    }
-    if (lane == 0) sh[64 + wid] = m;
-    __syncthreads();
-    if (wid == 0) {
-        int t[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) t[i] = lane < NWV ? sh[lane * 4 + i] : 0;
-#pragma unroll
-        for (int o = 1; o < NWV; o <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int y = __shfl_up(t[i], o, 64);
-                if (lane >= o) t[i] += y;
-            }
-        }
-        if (lane < NWV) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) sh[80 + lane * 4 + i] = t[i];
-        }
-        const int mm = wave_max(lane < NWV ? sh[64 + lane] : INT_MIN);
-        if (lane == 0) sh[80 + 4 * NWV] = mm;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        excl[i] = x[i] - v[i] + (wid > 0 ? sh[80 + (wid - 1) * 4 + i] : 0);
-        total[i] = sh[80 + (NWV - 1) * 4 + i];
-    }
-    *maxv = sh[80 + 4 * NWV];
-    __syncthreads();
-}
-
 // Which gate/up kernel takes the light tiles: the split-reduction one when sparse_rows > 0 and
 // the light tiles hold fewer than sparse_rows rows on average (the cold experts of a
 // concentrated batch, one or two rows each), else the streaming one.  Decided here from the real
@@ -147,12 +94,15 @@ __device__ __forceinline__ void write_light_split(DevHeader* hdr, int n_light, i
 // chunk c) into the first grouped row of (e, c); writes counts, offsets, the row tiles and
 // the header.  Thread t works on expert e = t % El' and part p = t / El' of its chunks
 // (El' = El rounded up to a power of two, P = kScanThreads / El' parts), so consecutive
-// threads read consecutive experts of a chunk.
+// threads read consecutive experts of a chunk.  The scan over the experts (grouped rows, light
+// and heavy tiles before each expert) is one wavefront's: lane j takes experts j*J .. j*J+J-1
+// (J = ceil(El/64)) in order, then one wavefront scan adds the lanes' sums.  dropped is read by
+// wavefront 0 only.
 __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int light_cap, int heavy_rows,
                               int rows_estimate, int sparse_rows, long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
-                              int* sh /* >= kScanShared ints */) {
+                              int* sh /* >= scan_lds_ints(El) ints */) {
     int Ep = 1;
     while (Ep < El) Ep <<= 1;
     const int P = kScanThreads / Ep;  // parts per expert (>= 1 since El <= 1024)
@@ -172,11 +122,11 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
         }
         for (; c < c1; c++) s += cnt[c * El + e];
     }
-    int* part_sum = sh + kScanLds;  // [kScanThreads], later 3 x [512]
-    static_assert(kScanLds + 3 * 512 <= kScanShared - 1, "light-row sum clear of the part sums");
-    int* light_rows = sh + kScanShared - 1;  // rows of the light tiles (LDS atomic sum)
+    int* part_sum = sh;               // [kScanThreads]
+    int* e_rows = sh + kScanThreads;  // [El]: rows of expert e, then its first grouped row
+    int* e_light = e_rows + El;       // [El]: its light tiles, then the light tiles before it
+    int* e_heavy = e_light + El;      // [El]: its heavy tiles, then the heavy tiles before it
     part_sum[threadIdx.x] = s;
-    if (threadIdx.x == 0) *light_rows = 0;
     __syncthreads();
     int before = 0, total = 0;  // this part's prefix inside its expert, and the expert total
     for (int q = 0; q < P; q++) {
@@ -184,7 +134,6 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
         if (q < part) before += v;
         total += v;
     }
-    const int lead = (live && part == 0);
     // an expert with 1..light_cap rows is cut into light tiles of tile_rows rows (the last one
     // takes the rest); a heavier one is cut into ceil(total / heavy_rows) tiles of equal size
     // rounded up to 16 rows (the last one takes the rest), so the tiles of one expert carry
@@ -194,39 +143,68 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
     const int nheavy0 = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
     const int hrows = heavy ? min(heavy_rows, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
     const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0
-    if (lead && !heavy && total > 0) atomicAdd(light_rows, total);  // read after the scan's barriers
-    int R, n_light, n_heavy, empty;
-    // grouped rows, light tiles, heavy tiles and empty experts before each expert (valid in
-    // its lead thread), their totals, and the largest expert
-    int first, lfirst, hfirst, max_rows;
-    {
-        const int vals[4] = {lead ? total : 0, lead ? nlight : 0, lead ? nheavy : 0, lead && total == 0};
-        int ex[4], tot[4];
-        block_scan4_max(vals, lead ? total : 0, sh, ex, tot, &max_rows);
-        first = ex[0];
-        lfirst = ex[1];
-        hfirst = ex[2];
-        R = tot[0];
-        n_light = tot[1];
-        n_heavy = tot[2];
-        empty = tot[3];
+    if (live && part == 0) {
+        e_rows[e] = total;
+        e_light[e] = nlight;
+        e_heavy[e] = nheavy;
     }
-    // hand the lead thread's expert offset and first tiles to the other parts of the expert
-    int* e_first = part_sum;           // [Ep]  (P > 1 means Ep <= 512; with P == 1 these are
-    int* e_lfirst = part_sum + 512;    // [Ep]   never written)
-    int* e_hfirst = part_sum + 1024;   // [Ep]
-    if (P > 1) {
-        if (lead) {
-            e_first[e] = first;
-            e_lfirst[e] = lfirst;
-            e_hfirst[e] = hfirst;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int J = (El + 63) >> 6;
+        const int ea = min(El, lane * J), eb = min(El, ea + J);
+        int sr = 0, sl = 0, sh_ = 0, lrows = 0, empty = 0, mx = 0;
+        for (int x = ea; x < eb; x++) {
+            const int r = e_rows[x], l = e_light[x];
+            sr += r;
+            sl += l;
+            sh_ += e_heavy[x];
+            lrows += l > 0 ? r : 0;
+            empty += r == 0;
+            mx = max(mx, r);
         }
-        __syncthreads();
+        // inclusive scans of the lanes' sums (rows, light tiles, heavy tiles, light rows, empty experts)
+        int ir = sr, il = sl, ih = sh_, ilr = lrows, ie = empty;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int yr = __shfl_up(ir, o, 64), yl = __shfl_up(il, o, 64), yh = __shfl_up(ih, o, 64);
+            const int ylr = __shfl_up(ilr, o, 64), ye = __shfl_up(ie, o, 64);
+            if (lane >= o) {
+                ir += yr;
+                il += yl;
+                ih += yh;
+                ilr += ylr;
+                ie += ye;
+            }
+        }
+        mx = wave_max(mx);
+        int fr = ir - sr, fl = il - sl, fh = ih - sh_;  // before this lane's first expert
+        for (int x = ea; x < eb; x++) {
+            const int r = e_rows[x], l = e_light[x], h = e_heavy[x];
+            e_rows[x] = fr;
+            e_light[x] = fl;
+            e_heavy[x] = fh;
+            fr += r;
+            fl += l;
+            fh += h;
+        }
+        if (lane == 63) {
+            offsets[El] = ir;
+            hdr->m_tiles = il;
+            hdr->m_tiles_heavy = ih;
+            hdr->local_rows = ir;
+            hdr->max_rows = mx;
+            hdr->empty_experts = ie;
+            hdr->dropped = dropped;
+            hdr->tile_rows = tile_rows;
+            hdr->heavy_rows = heavy_rows;
+            hdr->rows_estimate = rows_estimate;
+            write_light_split(hdr, il, ilr, sparse_rows);
+        }
     }
-    const int my_first = (P > 1) ? (live ? e_first[e] : 0) : first;
-    const int my_lfirst = (P > 1) ? (live ? e_lfirst[e] : 0) : lfirst;
-    const int my_hfirst = (P > 1) ? (live ? e_hfirst[e] : 0) : hfirst;
+    __syncthreads();
     if (live) {
+        const int my_first = e_rows[e], my_lfirst = e_light[e], my_hfirst = e_heavy[e];
         int run = my_first + before;
         int c = c0;
         for (; c + 8 <= c1; c += 8) {
@@ -246,7 +224,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
         }
         if (part == 0) {
             counts[e] = total;
-            offsets[e] = first;
+            offsets[e] = my_first;
         }
         // row tiles of expert e (split over its P threads)
         for (int j = part; j < nlight; j += P) {
@@ -268,19 +246,6 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
                 mtiles_heavy[my_hfirst + j] = mt;
             }
         }
-    }
-    if (threadIdx.x == 0) {
-        offsets[El] = R;
-        hdr->m_tiles = n_light;
-        hdr->m_tiles_heavy = n_heavy;
-        hdr->local_rows = R;
-        hdr->max_rows = max_rows;
-        hdr->empty_experts = empty;
-        hdr->dropped = dropped;
-        hdr->tile_rows = tile_rows;
-        hdr->heavy_rows = heavy_rows;
-        hdr->rows_estimate = rows_estimate;
-        write_light_split(hdr, n_light, *light_rows, sparse_rows);
     }
 }
 
@@ -311,7 +276,7 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
     int* cnt = lds;                        // [nchunk][El]
     int* mask = cnt + El * nchunk;         // [NW][El]
     int* bads = mask + NW * El;            // [kSmallChunks]
-    int* sh = bads + kSmallChunks;         // scan scratch [kScanShared]
+    int* sh = bads + kSmallChunks;         // scan scratch [scan_lds_ints(El)]
     const int w = threadIdx.x >> 6;
     // wavefront w ranks chunks w, w + NW, ...; the ids of all its chunks are loaded first, so
     // the wavefront waits for memory once rather than once per chunk
@@ -334,8 +299,14 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
         }
     }
     __syncthreads();
-    long long dropped = 0;
-    for (int c = 0; c < nchunk; c++) dropped += bads[c];
+    long long dropped = 0;  // wavefront 0 only (the one that writes the header)
+    if (w == 0) {
+        int d = 0;
+        for (int c = lane_id(); c < nchunk; c += 64) d += bads[c];  // <= 64 per chunk, <= 64 chunks
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
+        dropped = d;
+    }
     scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
                   mtiles_heavy, hdr, sh);
     __syncthreads();
@@ -349,7 +320,7 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
 
 static size_t small_lds_ints(int n, int El) {
     const int nchunk = (n + 63) / 64;
-    return (size_t)El * nchunk + (size_t)(kScanThreads / 64) * El + kSmallChunks + kScanShared;
+    return (size_t)El * nchunk + (size_t)(kScanThreads / 64) * El + kSmallChunks + scan_lds_ints(El);
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
@@ -491,7 +462,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
                                                             DevHeader* __restrict__ hdr) {
-    __shared__ int sh[kScanShared];
+    __shared__ int sh[scan_lds_ints(kScanThreads)];  // El <= kScanThreads (1024 local experts at most)
     __shared__ long long dsum[kScanThreads / 64];
     long long d = 0;
     for (int c = threadIdx.x; c < nchunk; c += kScanThreads) d += bad_buf[c];
