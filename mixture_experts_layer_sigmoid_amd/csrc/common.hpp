@@ -64,6 +64,16 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// SwiGLU's activation of one feature: SiLU(g) * u = g * u / (1 + e^-g), with e^-g as the hardware
+// 2^(-g log2 e) and the hardware reciprocal (each within a few ulp of the correctly rounded
+// value, far inside the bf16 rounding of h).  Below g of about -88, e^-g overflows to infinity
+// and the result is 0, the limit.  Every GEMM kernel uses this one definition, so the light and
+// heavy kernels agree bit for bit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 // One group of 128 values quantised by one wavefront, two values per lane (a, b: elements 2l
 // and 2l+1 of lane l): amax = max|v| (NaN ignored, as fmaxf does), s = amax/448 (1 for an
 // all-zero group), inv = 1/s, code = e4m3(clamp(v*inv, +-448)).  The clamp uses fminf/fmaxf,

@@ -62,7 +62,6 @@ struct StreamLds {
     float wsc[2][2][CS];        // FP8: weight-block scale of each matrix and step
 };
 
-__device__ __forceinline__ float silu_mul_s(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // a[i] for a runtime i, as a mask-and-or over the elements.  An indexed read of a register
 // array goes through scratch memory, and the compiler may fold a chain of selects over the
@@ -285,7 +284,7 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
                 am[sb] = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    r[sb][i] = silu_mul_s(acc[sb][0][i], acc[sb][NW - 1][i]);
+                    r[sb][i] = silu_mul(acc[sb][0][i], acc[sb][NW - 1][i]);
                     am[sb] = fmaxf(am[sb], fabsf(r[sb][i]));
                 }
                 am[sb] = fmaxf(am[sb], __shfl_xor(am[sb], 16, 64));
@@ -319,7 +318,7 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             const size_t o = (size_t)(c.row0 + col) * g.N + n0 + kg * 4;
             float r[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul_s(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
+            for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
             if (OUT == kOutF32) {
                 *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
             } else {

@@ -79,7 +79,6 @@ __device__ __forceinline__ void tg_static_chain(F&& f) {
     }
 }
 
-__device__ __forceinline__ float tg_silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // position of piece c of stage row r
 __device__ __forceinline__ int tg_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
@@ -319,7 +318,7 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                     const size_t o = (size_t)(row0 + r) * g.N + f;
                     float v[4];
 #pragma unroll
-                    for (int e = 0; e < 4; e++) v[e] = GATED ? tg_silu_mul(acc[i][c][e], acc[i][c + 2][e]) : acc[i][c][e];
+                    for (int e = 0; e < 4; e++) v[e] = GATED ? silu_mul(acc[i][c][e], acc[i][c + 2][e]) : acc[i][c][e];
                     if (OUT_F32) {
                         *(f32x4*)((float*)g.out + o) = f32x4{v[0], v[1], v[2], v[3]};
                     } else {
