@@ -20,6 +20,14 @@
 // Every step issues the same loads (padding steps past the reduction end re-read the last
 // valid step, which hits in cache), so the compiler's static wait counts stay exact.
 //
+// Outputs are parked in LDS and written to global memory a few tasks at a time (and at the
+// end).  A wavefront's memory operations leave its counter in issue order, so a global store
+// holds back every weight load issued after it until the store is acknowledged, and the weight
+// ring waits for it.  A bf16 down GEMM with its stores left out ran 13% faster (T=256 of the
+// 128-expert layer: 73 against 84 us); storing once per OUTQ tasks pays that wait once per
+// OUTQ tasks, and not at all for a workgroup with at most OUTQ tasks.  Each wavefront parks and
+// stores only its own outputs, so no barrier is involved.
+//
 // FP8 gate/up may also quantise its output itself (the w8a8 scheme's per-row, per-128-column
 // activation scales): a workgroup of 8 wavefronts then holds all 128 features of one scale
 // group, the wavefronts combine their row maxima through LDS, and the codes and scales are
@@ -62,6 +70,18 @@ struct StreamLds {
     float wsc[2][2][CS];        // FP8: weight-block scale of each matrix and step
 };
 
+// Parked outputs of up to Q tasks per wavefront: each lane's piece of each 16-row sub-block
+// (bf16: 4 features, fp32: 4 features, e4m3: 4 codes), the task's first row, rows and this
+// wavefront's first feature, and (e4m3, wavefront 0) the scale of each row's 128-feature group.
+template <int OUT, int NS, int WV, int Q>
+struct StreamParked {
+    using T = typename std::conditional<OUT == kOutF32, f32x4,
+                                        typename std::conditional<OUT == kOutE4M3, uint32_t, uint2>::type>::type;
+    T v[Q][WV][NS][64];
+    int meta[Q][WV][3];
+    float sc[OUT == kOutE4M3 ? Q : 1][NS][16];
+};
+
 
 // a[i] for a runtime i, as a mask-and-or over the elements.  An indexed read of a register
 // array goes through scratch memory, and the compiler may fold a chain of selects over the
@@ -102,6 +122,10 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     static_assert(OUT != kOutE4M3 || (GATED && FP8 && FEAT == 128), "e4m3 output: one 128-feature group per workgroup");
     __shared__ StreamLds<FP8, NS, CS> L;
     __shared__ float QM[OUT == kOutE4M3 ? NS * WV * 16 : 1];  // row maxima of each wavefront's 16 features
+    // tasks parked before a store: 4, or 2 where the staging buffers are large (FP8 down GEMM with
+    // chunks of 6 steps), so that two workgroups still fit a CU's LDS
+    constexpr int OUTQ = sizeof(StreamLds<FP8, NS, CS>) > 40 * 1024 ? 2 : 4;
+    __shared__ StreamParked<OUT, NS, WV, OUTQ> SO;
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -273,8 +297,38 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             }
         }
     };
-    // lane holds token column sb*16 + r16 and features n0 + 4*kg + i
+    // Parked outputs: nout tasks so far; task j sits in slot j % OUTQ.  flush(n) stores slots
+    // 0 .. n-1 of this wavefront (rows past the task's end are not stored).
+    int nout = 0;
+    auto flush = [&](int n) {
+        for (int q = 0; q < n; q++) {
+            const int row0 = SO.meta[q][w][0], rows = SO.meta[q][w][1], n0 = SO.meta[q][w][2];
+#pragma unroll
+            for (int sb = 0; sb < NS; sb++) {
+                const int col = sb * 16 + r16;
+                if (col >= rows) continue;
+                const size_t row = (size_t)(row0 + col);
+                const auto v = SO.v[q][w][sb][lane];
+                if constexpr (OUT == kOutE4M3) {
+                    *(uint32_t*)((uint8_t*)g.out + row * g.N + n0 + kg * 4) = v;
+                    if (w == 0 && kg == 0) g.out_scale[row * (g.N >> 7) + (n0 >> 7)] = SO.sc[q][sb][r16];
+                } else if constexpr (OUT == kOutF32) {
+                    *(f32x4*)((float*)g.out + row * g.N + n0 + kg * 4) = v;
+                } else {
+                    *(uint2*)((uint16_t*)g.out + row * g.N + n0 + kg * 4) = v;
+                }
+            }
+        }
+    };
+    // lane holds token column sb*16 + r16 and features n0 + 4*kg + i; the results are parked in
+    // this wavefront's next slot, and every OUTQ tasks the slots are stored
     auto epilogue = [&](const CT& c, int n0) {
+        const int q = nout % OUTQ;
+        if (lane == 0) {
+            SO.meta[q][w][0] = c.row0;
+            SO.meta[q][w][1] = c.rows;
+            SO.meta[q][w][2] = n0;
+        }
         if constexpr (OUT == kOutE4M3) {
             // every wavefront of the workgroup runs the same tasks, so all reach this barrier;
             // QM is rewritten only after the next task's chunk barriers
@@ -294,8 +348,6 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             __syncthreads();
 #pragma unroll
             for (int sb = 0; sb < NS; sb++) {
-                const int col = sb * 16 + r16;
-                if (col >= c.rows) continue;
                 float m = 0.0f;
 #pragma unroll
                 for (int v = 0; v < WV; v++) m = fmaxf(m, QM[(sb * WV + v) * 16 + r16]);
@@ -304,30 +356,27 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
                 float y[4];
 #pragma unroll
                 for (int i = 0; i < 4; i++) y[i] = fmaxf(fminf(r[sb][i] * inv, kE4M3Max), -kE4M3Max);
-                const size_t row = (size_t)(c.row0 + col);
-                *(uint32_t*)((uint8_t*)g.out + row * g.N + n0 + kg * 4) =
-                    f32x2_to_e4m3x2(y[0], y[1]) | (f32x2_to_e4m3x2(y[2], y[3]) << 16);
-                if (w == 0 && kg == 0) g.out_scale[row * (g.N >> 7) + (n0 >> 7)] = sc;
+                SO.v[q][w][sb][lane] = f32x2_to_e4m3x2(y[0], y[1]) | (f32x2_to_e4m3x2(y[2], y[3]) << 16);
+                if (w == 0 && kg == 0) SO.sc[q][sb][r16] = sc;
             }
-            return;
-        }
+        } else {
 #pragma unroll
-        for (int sb = 0; sb < NS; sb++) {
-            const int col = sb * 16 + r16;
-            if (col >= c.rows) continue;
-            const size_t o = (size_t)(c.row0 + col) * g.N + n0 + kg * 4;
-            float r[4];
+            for (int sb = 0; sb < NS; sb++) {
+                float r[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) r[i] = GATED ? silu_mul(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
-            if (OUT == kOutF32) {
-                *(f32x4*)((float*)g.out + o) = f32x4{r[0], r[1], r[2], r[3]};
-            } else {
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
-                *(uint2*)((uint16_t*)g.out + o) = pk;
+                for (int i = 0; i < 4; i++)
+                    r[i] = GATED ? silu_mul(acc[sb][0][i], acc[sb][NW - 1][i]) : acc[sb][0][i];
+                if constexpr (OUT == kOutF32) {
+                    SO.v[q][w][sb][lane] = f32x4{r[0], r[1], r[2], r[3]};
+                } else {
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+                    pk.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+                    SO.v[q][w][sb][lane] = pk;
+                }
             }
         }
+        if (++nout % OUTQ == 0) flush(OUTQ);
     };
     auto task_n0 = [&](int i) {
         int mt, nb;
@@ -381,6 +430,7 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
         run_task(i, ca, cb);
         if (i + 1 < ntasks) run_task(i + 1, cb, ca);
     }
+    flush(nout % OUTQ);
 }
 
 // wavefronts per workgroup: 8 for the down GEMM (its short reduction makes the tile's staged
