@@ -122,8 +122,8 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     static_assert(OUT != kOutE4M3 || (GATED && FP8 && FEAT == 128), "e4m3 output: one 128-feature group per workgroup");
     __shared__ StreamLds<FP8, NS, CS> L;
     __shared__ float QM[OUT == kOutE4M3 ? NS * WV * 16 : 1];  // row maxima of each wavefront's 16 features
-    // tasks parked before a store: 4, or 2 where the staging buffers are large (FP8 down GEMM with
-    // chunks of 6 steps), so that two workgroups still fit a CU's LDS
+    // tasks parked before a store: 4, or 2 where the staging buffers are large (more than 40 KB),
+    // so that two workgroups still fit a CU's LDS
     constexpr int OUTQ = sizeof(StreamLds<FP8, NS, CS>) > 40 * 1024 ? 2 : 4;
     __shared__ StreamParked<OUT, NS, WV, OUTQ> SO;
 
@@ -459,10 +459,12 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
 }
 
 // Chunk length CS and weight ring depth D: bf16 8 and 8, FP8 4 and 4.  An FP8 down GEMM on
-// 32-row tiles whose reduction is a multiple of 6 steps (768 deep: 6 steps) takes chunks of 6
-// instead, so no chunk is padded past the reduction end (a third of the steps with chunks of
-// 4; measured 10% faster there), with a ring of 2 (measured ~1 us faster than a ring of 3
-// and 4-6 us faster than a ring of 6 at 64-256 tokens of the 128-expert layer).
+// 32-row tiles whose reduction is a multiple of 6 steps but not of 4 (768 deep: 6 steps) takes
+// chunks of 2 steps with a ring of 2 instead: no chunk is padded past the reduction end (chunks
+// of 4 pad a third of the steps; measured 10% slower), and a task spans several chunks, so the
+// next tasks' activations are staged from gather-map entries loaded a task earlier rather than
+// right after their load.  Chunks of 2 measured 1-1.5 us faster than one chunk of 6 at 64-256
+// tokens of the 128-expert layer; rings of 3 and 6 were no faster than 2.
 template <bool GATED, bool FP8, int OUT>
 hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, int cus, hipStream_t st) {
     constexpr int CS = SCfg<FP8>::CS, D = FP8 ? 4 : 8;
@@ -470,7 +472,7 @@ hipError_t launch_stream_rows(const GemmArgs& a, int tile_rows, int max_tiles, i
     if (tile_rows == 32) {
         if constexpr (FP8 && !GATED) {
             const int nsteps = a.K / SCfg<FP8>::KSTEP;
-            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT, 2, 6, 2>(a, max_tiles, cus, st);
+            if (nsteps % 6 == 0 && nsteps % CS != 0) return launch_stream<GATED, FP8, OUT, 2, 2, 2>(a, max_tiles, cus, st);
         }
         return launch_stream<GATED, FP8, OUT, 2, CS, D>(a, max_tiles, cus, st);
     }

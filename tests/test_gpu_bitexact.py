@@ -322,7 +322,7 @@ PLANS = {  # (tile rows, gate/up split, down split, light tiles per expert)
 }
 
 
-@pytest.mark.parametrize("H,I", [(256, 384), (640, 256), (1152, 896)])
+@pytest.mark.parametrize("H,I", [(256, 384), (640, 256), (1152, 896), (512, 768)])
 @pytest.mark.parametrize("plan", list(PLANS))
 @pytest.mark.parametrize("fp8", [False, True])
 def test_integer_grouped_gemm_is_bit_exact(fp8, plan, H, I):
