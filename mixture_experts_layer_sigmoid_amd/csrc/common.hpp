@@ -56,8 +56,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // fp32 -> OCP e4m3 code, round to nearest even with saturation (the gfx950 conversion
-// instruction; its rounding was checked against a software encoder on all 2^32 inputs
-// clamped to +-448).  Callers clamp to +-448 first.
+// instruction).  Callers clamp to +-448 first.  The GPU quantisation tests compare its codes
+// bit for bit with the oracle's own encoder at every rounding midpoint of the format, at both
+// fp32 neighbours of each midpoint, and on 2^20 random values spread over every binade.
 __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
