@@ -93,8 +93,9 @@ typedef struct {
                                 is one light tile, a heavier one heavy tiles (FP8 when every
                                 expert fits 8 light tiles: ceil(c / tile_rows) light tiles)  */
     int32_t heavy_tiles;     /* row tiles of the experts cut into heavy tiles               */
-    int32_t heavy_rows;      /* host plan: rows of a full heavy tile (an expert with c rows
-                                gets ceil(c / heavy_rows) tiles of about equal size)         */
+    int32_t heavy_rows;      /* largest heavy tile: 256 rows, an expert with c rows getting
+                                ceil(c / 256) tiles of about equal size; 320 when the grouping
+                                step cut every expert of 257..320 rows as one tile (bf16)    */
     int32_t light_rows;      /* rows of the light tiles                                     */
     int32_t split_light_tiles; /* light tiles whose gate/up GEMM ran on the split-reduction
                                 kernel because they held few rows on average (the grouping's
@@ -195,15 +196,21 @@ int fmoe_forward(const fmoe_shape* shape, const void* x, const void* logits, int
  *                  into heavy tiles) or 8 (experts of up to 8*tile_rows rows are cut into
  *                  light tiles, and the heavy-tile launches are left out when no expert can
  *                  hold more: at most T rows for router ids, T*top_k for caller ids); the
- *                  heuristic takes 8 for FP8 weights and 1 for bf16 */
+ *                  heuristic takes 8 for FP8 weights and 1 for bf16
+ *   heavy_rows     largest heavy tile: 256, or 320 (bf16 weights only): an expert of 257..320
+ *                  rows is then one tile of five 64-row groups instead of two tiles.  The
+ *                  heuristic decides on the device from the real counts: 320 when the heavy
+ *                  tiles of 256 rows give every compute unit at least four tasks in both
+ *                  GEMMs (a throughput-bound launch, where one task in place of two saves
+ *                  copies), else 256 (a longer task would lengthen the launch) */
 typedef struct {
-    int32_t tile_rows, split_gate_up, split_down, light_tiles;
+    int32_t tile_rows, split_gate_up, split_down, light_tiles, heavy_rows;
 } fmoe_plan;
 
 /* fmoe_forward with the nonzero fields of *plan (NULL: none) in place of the heuristic's
  * choices.  FMOE_ERR_ARG for a field outside the values above; FMOE_ERR_UNSUPPORTED when an
  * FP8 layer's 32-row tile would not fit the activation scales of a split tile in 64 KB of LDS
- * (the limit the heuristic also applies).  fmoe_workspace_bytes(shape) fits every plan.
+ * (the limit the heuristic also applies), or for heavy_rows 320 with FP8 weights.  fmoe_workspace_bytes(shape) fits every plan.
  * Results equal fmoe_forward's within the layer's rounding (the reduction order of a split
  * tile differs). */
 int fmoe_forward_planned(const fmoe_shape* shape, const void* x, const void* logits,

@@ -41,9 +41,10 @@ class fmoe_weights(ctypes.Structure):
 class fmoe_plan(ctypes.Structure):
     """Tile plan overrides (0 keeps the heuristic's choice): tile_rows 16/32, split_gate_up and
     split_down 1 (streaming kernel), 2 or 4 wavefronts per reduction, light_tiles 1 or 8 light
-    tiles per expert at most (8: heavy-tile launches left out when no expert can need more)."""
+    tiles per expert at most (8: heavy-tile launches left out when no expert can need more),
+    heavy_rows 256 or 320 (bf16: experts of 257..320 rows as one heavy tile of five row groups)."""
     _fields_ = [("tile_rows", ctypes.c_int32), ("split_gate_up", ctypes.c_int32), ("split_down", ctypes.c_int32),
-                ("light_tiles", ctypes.c_int32)]
+                ("light_tiles", ctypes.c_int32), ("heavy_rows", ctypes.c_int32)]
 
 
 class fmoe_layout(ctypes.Structure):

@@ -47,7 +47,7 @@ struct Plan {
     int tile_rows;       // largest light row tile: 16 or 32
     int light_cap;       // experts with up to this many rows get light tiles, heavier ones heavy tiles
     bool heavy_launch;   // some expert may exceed light_cap: run the heavy-tile kernels
-    int heavy_rows;      // rows of a full heavy tile
+    int heavy5;          // one tile for experts of 257..320 rows: -1 never, 1 always, 0 the grouping decides
     int max_light;       // bounds on light and heavy row tiles for any routing
     int max_heavy;
     int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
@@ -156,13 +156,13 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr, long long max
     p.light_cap = max_expert_rows <= (long long)per * tr ? per * tr : tr;
     p.heavy_launch = max_expert_rows > p.light_cap;
     // light tiles: ceil(c/tile_rows) per expert with 1..light_cap rows, at most
-    // min(n, El + n/16) in all; heavy tiles: ceil(c/heavy_rows) per expert with c > tile_rows
-    // rows, at most n/heavy_rows + n/(tile_rows+1) in all (bounded with the smallest light tile,
+    // min(n, El + n/16) in all; heavy tiles: at most ceil(c/256) per expert with c > tile_rows
+    // rows, at most n/256 + n/(tile_rows+1) in all (bounded with the smallest light tile,
     // 16 rows, so one workspace fits every tile plan); no tile is empty
     long long nl = p.El + p.n / 16;
     if (nl > p.n) nl = p.n;
-    p.heavy_rows = heavy_max_rows(p.fp8);
-    long long nh = p.n / p.heavy_rows + (p.n / 17 < p.El ? p.n / 17 : p.El) + 1;
+    p.heavy5 = p.fp8 ? -1 : ov && ov->heavy_rows ? (ov->heavy_rows == kHeavyRows5 ? 1 : -1) : 0;
+    long long nh = p.n / kHeavyRows + (p.n / 17 < p.El ? p.n / 17 : p.El) + 1;
     if (nh > p.n) nh = p.n;
     p.max_light = (int)(nl < 1 ? 1 : nl);
     p.max_heavy = (int)(nh < 1 ? 1 : nh);
@@ -222,14 +222,28 @@ bool log_enabled() {
     return on != 0;
 }
 
+// The 256-row heavy tiles from which the grouping cuts an expert of 257..320 rows as one tile
+// of five row groups (INT_MAX: never): enough tiles that the GEMM with the fewer 128-column
+// blocks (gate/up 2*I/128, down H/128) gives every compute unit four tasks.  There the launch is
+// bound by the copies into LDS, which one task in place of two cuts by the second task's weight
+// stream (128 experts of 272 rows, 2048 deep: 290 against 360 us for the gate/up GEMM as one
+// tile and as two); with fewer tasks the launch is as long as its longest task, which a tile of
+// five groups lengthens (the hot experts of a concentrated batch: 81 against 64 us).
+int heavy5_min_tiles(const Plan& p) {
+    if (p.heavy5 < 0) return INT_MAX;
+    if (p.heavy5 > 0) return 0;
+    const int nb = 2 * p.I < p.H ? 2 * p.I / 128 : p.H / 128;
+    return (4 * device_cus() + nb - 1) / nb;
+}
+
 void log_plan(const char* who, const Plan& p) {
     if (!log_enabled()) return;
     std::fprintf(stderr,
                  "[fmoe] %s: T=%d H=%d I=%d E=%d k=%d E_loc=%d first_expert=%d %s | rows_estimate=%d "
-                 "tile_rows=%d light_cap=%d heavy_launch=%d heavy_rows=%d split_gate_up=%d split_down=%d "
+                 "tile_rows=%d light_cap=%d heavy_launch=%d heavy5=%d split_gate_up=%d split_down=%d "
                  "sparse_rows=%d max_light_tiles=%d max_heavy_tiles=%d workspace=%zu B\n",
                  who, p.T, p.H, p.I, p.E, p.k, p.El, p.lo, p.fp8 ? "fp8" : "bf16", p.rows_estimate, p.tile_rows,
-                 p.light_cap, (int)p.heavy_launch, p.heavy_rows, p.wk1, p.wk2, p.sparse_rows, p.max_light, p.max_heavy,
+                 p.light_cap, (int)p.heavy_launch, p.heavy5, p.wk1, p.wk2, p.sparse_rows, p.max_light, p.max_heavy,
                  p.L.total);
 }
 
@@ -269,7 +283,7 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
     record(ev, FMOE_STAGE_GROUP, st);
     MTile* mtiles_heavy = mtiles + p.max_light;
     if (!grouped)
-        FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate,
+        FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, heavy5_min_tiles(p), p.rows_estimate,
                               p.sparse_rows, (int32_t*)(ws + L.counts),
                           (int32_t*)(ws + L.offsets), perm, inv, (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles,
                           mtiles_heavy, hdr, st));
@@ -363,7 +377,7 @@ int run_stage(const Plan& p, int stage, const int32_t* ids, const void* a, const
     MTile* mtiles = (MTile*)(ws + L.mtiles);
     MTile* mtiles_heavy = mtiles + p.max_light;
     const int cus = device_cus();
-    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate, 0,
+    FMOE_TRY(launch_group(ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, heavy5_min_tiles(p), p.rows_estimate, 0,
                           (int32_t*)(ws + L.counts), (int32_t*)(ws + L.offsets), perm, (int32_t*)(ws + L.inv),
                           (int32_t*)(ws + L.rank), (int*)(ws + L.grp), mtiles, mtiles_heavy, hdr, st));
     GemmArgs g;
@@ -421,6 +435,8 @@ int check_plan(const fmoe_shape* s, const fmoe_plan* ov) {
     if (!(ov->tile_rows == 0 || ov->tile_rows == 16 || ov->tile_rows == 32)) return FMOE_ERR_ARG;
     if (!split_ok(ov->split_gate_up) || !split_ok(ov->split_down)) return FMOE_ERR_ARG;
     if (!(ov->light_tiles == 0 || ov->light_tiles == 1 || ov->light_tiles == kMaxLightPerExpert)) return FMOE_ERR_ARG;
+    if (!(ov->heavy_rows == 0 || ov->heavy_rows == kHeavyRows || ov->heavy_rows == kHeavyRows5)) return FMOE_ERR_ARG;
+    if (s->weight_dtype == FMOE_FP8_E4M3 && ov->heavy_rows == kHeavyRows5) return FMOE_ERR_UNSUPPORTED;
     const int K = s->hidden > s->inter ? s->hidden : s->inter;
     if (s->weight_dtype == FMOE_FP8_E4M3 && ov->tile_rows == 32 && gemm_lds_bytes(true, K, 32) > 65536)
         return FMOE_ERR_UNSUPPORTED;
@@ -455,7 +471,7 @@ int forward_impl(const fmoe_shape* s, const void* x, const void* logits, int32_t
         const Layout& L = p.L;
         MTile* mtiles = (MTile*)(wsb + L.mtiles);
         FMOE_TRY(launch_route_group(logits, bf16, (int)p.T, p.E, p.k, scoring, renormalize != 0, ids, wts, p.El, p.lo,
-                                    p.tile_rows, p.light_cap, p.heavy_rows, p.rows_estimate, p.sparse_rows,
+                                    p.tile_rows, p.light_cap, heavy5_min_tiles(p), p.rows_estimate, p.sparse_rows,
                                     (int32_t*)(wsb + L.counts),
                                     (int32_t*)(wsb + L.offsets), (int32_t*)(wsb + L.perm), (int32_t*)(wsb + L.inv),
                                     mtiles, mtiles + p.max_light, (DevHeader*)(wsb + L.hdr), st, xqp));
@@ -566,7 +582,7 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
     if (ws_bytes < p.L.total) return FMOE_ERR_WORKSPACE;
     char* wsb = (char*)ws;
     MTile* mt = (MTile*)(wsb + p.L.mtiles);
-    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, p.heavy_rows,
+    return hip_status(launch_group(topk_ids, (int)p.n, p.E, p.El, p.lo, p.tile_rows, p.light_cap, heavy5_min_tiles(p),
                                    p.rows_estimate, p.sparse_rows, counts, offsets,
                                    perm_src, inv_perm, (int32_t*)(wsb + p.L.rank), (int*)(wsb + p.L.grp), mt,
                                    mt + p.max_light, (DevHeader*)(wsb + p.L.hdr), (hipStream_t)stream));

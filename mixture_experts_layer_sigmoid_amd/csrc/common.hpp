@@ -15,8 +15,10 @@ constexpr float kE4M3Max = 448.0f;  // largest finite OCP E4M3FN magnitude
 constexpr int kMaxKBlocks = 512;    // 128-deep blocks of the reduction dimension (65536 / 128)
 constexpr int kLightRows = 32;      // largest row tile of the light GEMM kernel
 constexpr int kMaxLightPerExpert = 8;  // light tiles of one expert when heavy tiles are left out
-// largest row tile of the heavy GEMM kernel (4 groups of 64 rows)
-constexpr int heavy_max_rows(bool) { return 256; }
+// row tiles of the heavy GEMM kernel: 4 groups of 64 rows, or 5 for an expert of 257..320
+// rows in one tile (bf16 only: FP8's activation scales take LDS that a fifth group would need)
+constexpr int kHeavyRows = 256;
+constexpr int kHeavyRows5 = 320;
 
 // Workspace header written by the grouping kernel and read by later kernels and by
 // fmoe_read_stats.  Field order is part of the workspace format of this library only.
@@ -29,7 +31,7 @@ struct DevHeader {
     int32_t tile_rows;      // largest rows per tile used to cut the experts
     int32_t rows_estimate;  // max(1, ceil(T*top_k/E)) of the host plan
     int32_t m_tiles_heavy;  // heavy row tiles (experts with more than the light limit)
-    int32_t heavy_rows;     // rows of a full heavy tile
+    int32_t heavy_rows;     // largest heavy tile: kHeavyRows, or kHeavyRows5 when used
     int32_t light_rows;     // rows of the light tiles
     int32_t m_tiles_stream; // light tiles of the streaming gate/up kernel (all or none of them)
     int32_t m_tiles_split;  // light tiles of the split-reduction gate/up kernel (the others)

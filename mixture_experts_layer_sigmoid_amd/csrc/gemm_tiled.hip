@@ -4,22 +4,22 @@
 // for experts that hold more rows than a light tile: large batches, and the hot experts of a
 // concentrated routing ("vLLM Community Traces H20 MoE Scheduling Inefficiency to
 // Expert-Load Kernel Selection", paragraph 4: concentrated routing needs another kernel choice
-// than the average).  With up to 256 rows per tile the work is a dense contraction, so the
+// than the average).  With up to 320 rows per tile the work is a dense contraction, so the
 // kernel is built around the matrix cores rather than the weight stream.
 //
-// Shape: one workgroup of 8 wavefronts computes a tile of up to 256 rows times 128 weight
-// columns (gate/up: 64 features of each matrix, so SiLU-and-mul happens in registers).  The
-// tile's rows are staged in NA groups of 64 (NA = 1..4); the wavefronts form a 4 x 2 grid, each
+// Shape: one workgroup of 8 wavefronts computes a tile of up to 320 rows (FP8: 256) times 128
+// weight columns (gate/up: 64 features of each matrix, so SiLU-and-mul happens in registers).
+// The tile's rows are staged in NA groups of 64 (NA = 1..5, FP8 1..4); the wavefronts form a 4 x 2 grid, each
 // owning 16*NA rows x 64 columns (4*NA accumulators of 16 x 16), so all 8 wavefronts, and all
 // four SIMDs equally, carry MFMA work whatever the tile's size.
 // Every 128-byte slice of the reduction (64 bf16 or 128 e4m3 per row) is one stage: the
 // activation rows (gathered through the row map) and the weight rows are copied straight from
-// global memory into LDS by direct global-to-LDS loads: the activations three stages deep, the
-// weights four stages deep for bf16 (160 KB in all) and three for FP8, so two activation and
-// three (FP8: two) weight stages are in flight while one is read.  A stage row of 8 pieces of 16 bytes keeps piece c at position
-// c ^ ((row >> 1) & 7): the 16 rows read by one MFMA fragment then fall in 16 different bank
-// groups.  Each buffer is a separate LDS array and every wait is an explicit count of the loads
-// that must have landed, so the compiler never has to wait for loads into another buffer.
+// global memory into LDS by direct global-to-LDS loads: the activations three stages deep (two
+// for tiles of five row groups), the weights four stages deep for bf16 (160 KB in all) and three
+// for FP8, so one or two activation and three (FP8: two) weight stages are in flight while one is
+// read.  A stage row of 8 pieces of 16 bytes keeps piece c at position c ^ ((row >> 1) & 7): the
+// 16 rows read by one MFMA fragment then fall in 16 different bank groups.  Every wait is an
+// explicit count of the loads that must have landed.
 //
 // Per stage and wavefront (NA = 4): 8 fragment reads (16 KB) feed 32 MFMAs of 16x16x32 (bf16),
 // or 4 + 4 double-width reads feed 16 MFMAs of 16x16x128 (FP8, one per 128-deep scale block,
@@ -37,14 +37,36 @@ namespace fmoe {
 
 namespace {
 
-constexpr int kTgRows = 256;     // rows of a tile at most
 constexpr int kTgCols = 128;     // weight columns per workgroup
 constexpr int kTgThreads = 512;  // 8 wavefronts
-constexpr int kTgXPieces = kTgRows * 8;  // 16-byte pieces of one activation stage
-constexpr int kTgWPieces = kTgCols * 8;  // 16-byte pieces of one weight stage
+constexpr int kTgWPieces = kTgCols * 8;  // 16-byte pieces of one weight stage (16 KB)
+constexpr int kTgPieces = 10240;         // 16-byte pieces of the LDS (160 KB)
+// LDS layout for a tile of NA 64-row groups (16-byte pieces): NX activation buffers of
+// tg_xstride pieces (NA <= 4: three of 32 KB; NA = 5, bf16 only: two of 40 KB), then the
+// weight buffers of 16 KB (bf16: four, FP8: three), then (FP8) three buffers of 256 fp32
+// activation scales.
+template <int NA> constexpr int tg_nx() { return NA == 5 ? 2 : 3; }
+template <int NA> constexpr int tg_xstride() { return NA == 5 ? 5 * 512 : 4 * 512; }
+template <int NA> constexpr int tg_wbase() { return tg_nx<NA>() * tg_xstride<NA>(); }
+constexpr int kTgSBase = 3 * 2048 + 3 * kTgWPieces;
+static_assert(tg_wbase<4>() + 4 * kTgWPieces <= kTgPieces && tg_wbase<5>() + 4 * kTgWPieces <= kTgPieces &&
+                  kTgSBase + 3 * 64 <= kTgPieces,
+              "LDS layout");
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
+// Global-to-LDS copies of 64 lanes (16 or 4 bytes each) to LDS byte address lds (wavefront-
+// uniform, in M0, which nothing else in this kernel uses).  Written as inline assembly: the
+// buffers are parts of one LDS array picked per tile size, and the compiler, which tracks its
+// own copies per array, would otherwise wait for every copy into the array before each
+// fragment read.  Every wait on these copies is an explicit count.  No memory clobber: a copy
+// never writes a buffer read in the same step, and as volatile statements the copies keep
+// their order against the stage barrier and the waits; the fragment reads of the current
+// stage may then be scheduled among them.
+__device__ __forceinline__ void tg_copy16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "m0");
+}
+__device__ __forceinline__ void tg_copy4(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(src) : "m0");
+}
 
 template <int N>
 __device__ __forceinline__ void tg_wait_vmcnt() {
@@ -85,12 +107,12 @@ __device__ __forceinline__ int tg_slot(int r, int c) { return r * 8 + (c ^ ((r >
 
 template <bool GATED, bool FP8, bool OUT_F32>
 __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
-    // bf16: three activation and four weight buffers, 3 x 32 KB + 4 x 16 KB = 160 KB of LDS;
-    // FP8 keeps three weight buffers (its activation scales take the room of the fourth)
+    // bf16: three activation and four weight buffers, 3 x 32 KB + 4 x 16 KB = 160 KB of LDS
+    // (tiles of five row groups: two of 40 KB and four); FP8 keeps three weight buffers (its
+    // activation scales take the room of the fourth)
     constexpr int NW = FP8 ? 3 : 4;
-    __shared__ i32x4 X0[kTgXPieces], X1[kTgXPieces], X2[kTgXPieces];
-    __shared__ i32x4 W0[kTgWPieces], W1[kTgWPieces], W2[kTgWPieces], W3[NW > 3 ? kTgWPieces : 1];
-    __shared__ float SA0[FP8 ? kTgRows : 1], SA1[FP8 ? kTgRows : 1], SA2[FP8 ? kTgRows : 1];
+    __shared__ i32x4 LDS[kTgPieces];
+    const uint32_t lds0 = (uint32_t)(size_t)(void*)LDS;
 
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -137,6 +159,9 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
             constexpr int NA = decltype(NAc)::value;  // activation loads per stage = 64-row groups
             constexpr int LX = NA + (FP8 ? 1 : 0);  // vector-memory instructions per activation stage
             constexpr int LW = 2;                   // and per weight stage
+            constexpr int NX = tg_nx<NA>();         // activation buffers
+            constexpr int XSTRIDE = tg_xstride<NA>(), WBASE = tg_wbase<NA>();
+            static_assert(!FP8 || NA <= 4, "FP8 tiles have at most 256 rows");
             // activation pieces: load j of wavefront w covers stage rows (j*8 + w)*8 .. +8
             size_t xoff[NA];
 #pragma unroll
@@ -175,27 +200,22 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
             // activation stage kb into buffer X<B> (FP8: with its activation scales)
             auto issue_x = [&](auto Bc, int kb) {
                 constexpr int B = decltype(Bc)::value;
-                i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
+                const uint32_t X = lds0 + (uint32_t)(B * XSTRIDE) * 16;
                 const size_t ko = (size_t)kb * 128;
 #pragma unroll
                 for (int j = 0; j < NA; j++)
-                    __builtin_amdgcn_global_load_lds((gbl_void*)((const uint8_t*)g.A + xoff[j] + ko),
-                                                     (lds_void*)(X + (j * 8 + w) * 64), 16, 0, 0);
-                if constexpr (FP8) {
-                    float* S = B == 0 ? SA0 : B == 1 ? SA1 : SA2;
-                    __builtin_amdgcn_global_load_lds((gbl_void*)(g.A_scale + (size_t)ssrc * nkb128 + kb),
-                                                     (lds_void*)(S + (w & 3) * 64), 4, 0, 0);
-                }
+                    tg_copy16((const uint8_t*)g.A + xoff[j] + ko, X + (uint32_t)((j * 8 + w) * 64) * 16);
+                if constexpr (FP8)
+                    tg_copy4(g.A_scale + (size_t)ssrc * nkb128 + kb,
+                             lds0 + (uint32_t)(kTgSBase + B * 64) * 16 + (uint32_t)(w & 3) * 64 * 4);
             };
             // weight stage kb into buffer W<B>
             auto issue_w = [&](auto Bc, int kb) {
                 constexpr int B = decltype(Bc)::value;
-                i32x4* W = B == 0 ? W0 : B == 1 ? W1 : B == 2 ? W2 : W3;
+                const uint32_t W = lds0 + (uint32_t)(WBASE + B * kTgWPieces) * 16;
                 const size_t ko = (size_t)kb * 128;
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    __builtin_amdgcn_global_load_lds((gbl_void*)(wsrc[j] + ko), (lds_void*)(W + (j * 8 + w) * 64), 16,
-                                                     0, 0);
+                for (int j = 0; j < 2; j++) tg_copy16(wsrc[j] + ko, W + (uint32_t)((j * 8 + w) * 64) * 16);
             };
 
             f32x4 acc[NA][4];
@@ -211,10 +231,12 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
             const int fb = GATED ? nb / 2 : nb;
             const size_t sidx = ((size_t)expert * (g.N / 128) + fb) * nkb128;
 
-            auto compute = [&](auto BXc, auto BWc, int kb) {
+            // issue(): the next stages' copies, placed after this stage's fragment reads so that
+            // every wavefront starts its MFMAs before its copies queue up behind the others'
+            auto compute = [&](auto BXc, auto BWc, int kb, auto issue) {
                 constexpr int B = decltype(BXc)::value, BW = decltype(BWc)::value;
-                const i32x4* X = B == 0 ? X0 : B == 1 ? X1 : X2;
-                const i32x4* W = BW == 0 ? W0 : BW == 1 ? W1 : BW == 2 ? W2 : W3;
+                const i32x4* X = LDS + B * XSTRIDE;
+                const i32x4* W = LDS + WBASE + BW * kTgWPieces;
                 if constexpr (!FP8) {
 #pragma unroll
                     for (int q = 0; q < 2; q++) {
@@ -224,6 +246,7 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                             xa[i] = __builtin_bit_cast(bf16x8, X[(rb0 + i * 16) * 8 + frag[q]]);
 #pragma unroll
                         for (int c = 0; c < 4; c++) wb[c] = __builtin_bit_cast(bf16x8, W[wcol(c) * 8 + frag[q]]);
+                        if (q == 1) issue();
 #pragma unroll
                         for (int i = 0; i < NA; i++)
 #pragma unroll
@@ -231,7 +254,7 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                                 acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[c], xa[i], acc[i][c], 0, 0, 0);
                     }
                 } else {
-                    const float* S = B == 0 ? SA0 : B == 1 ? SA1 : SA2;
+                    const float* S = (const float*)(LDS + kTgSBase + B * 64);
                     const float ws0 = *(const __attribute__((address_space(4))) float*)(g.S0 + sidx + kb);
                     const float ws1 =
                         GATED ? *(const __attribute__((address_space(4))) float*)(g.S1 + sidx + kb) : ws0;
@@ -246,6 +269,7 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                         const i32x4 lo = W[wcol(c) * 8 + frag[0]], hi = W[wcol(c) * 8 + frag[1]];
                         wb[c] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                     }
+                    issue();
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < NA; i++) {
@@ -262,25 +286,39 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
                 }
             };
 
-            // Stage s sits in X<s % 3> and W<s % NW>.  The step of stage s waits for it (this
+            // Stage s sits in X<s % NX> and W<s % NW>.  The step of stage s waits for it (this
             // wavefront's loads, then everyone's), which also means every wavefront is done with
-            // stage s-1, whose buffers then take activation stage s+2 and weight stage s+NW-1:
-            // with four weight buffers the weights run one stage further ahead than the
-            // activations.  Loads land in issue order, so the wait is a count of the loads issued
-            // after the last one of stage s: NW = 3 (issue order X2 W2 X3 W3 ..): the next step's
-            // X and W; NW = 4 (W0 X0 W1 X1 W2, then X2 W3 X3 W4 ..): a W, then the next X and W.
-            // The last steps reload the last stage (from L2) in place of the stages past the end.
-            constexpr int WAIT = NW == 3 ? LX + LW : LX + 2 * LW;
+            // stage s-1, whose buffers then take activation stage s+NX-1 and weight stage s+NW-1:
+            // the weights run one or two stages further ahead than the activations.  Loads land in
+            // issue order, so the wait is a count of the loads issued after the last one of stage
+            // s: NX = 3, NW = 3 (issue order X0 W0 X1 W1, then X2 W2 X3 W3 ..): the next step's X
+            // and W; NX = 3, NW = 4 (W0 X0 W1 X1 W2, then X2 W3 X3 W4 ..): a W, then the next X
+            // and W; NX = 2, NW = 4 (W0 W1 X0 W2, then X1 W3 X2 W4 ..): the next step's W.  The
+            // last steps reload the last stage (from L2) in place of the stages past the end.
+            constexpr int WAIT = NX == 2 ? LW : NW == 3 ? LX + LW : LX + 2 * LW;
             auto step = [&](auto Jc, int kb) {
                 constexpr int J = decltype(Jc)::value;
                 tg_wait_vmcnt<WAIT>();
                 tg_barrier();
-                issue_x(std::integral_constant<int, (J + 2) % 3>{}, min(kb + 2, nkb - 1));
-                issue_w(std::integral_constant<int, (J + NW - 1) % NW>{}, min(kb + NW - 1, nkb - 1));
-                compute(std::integral_constant<int, J % 3>{}, std::integral_constant<int, J % NW>{}, kb);
+                auto issue = [&] {
+                    issue_x(std::integral_constant<int, (J + NX - 1) % NX>{}, min(kb + NX - 1, nkb - 1));
+                    issue_w(std::integral_constant<int, (J + NW - 1) % NW>{}, min(kb + NW - 1, nkb - 1));
+                };
+                // with two activation buffers a copy has one stage to land: issue it first
+                if constexpr (NX == 2) {
+                    issue();
+                    compute(std::integral_constant<int, J % NX>{}, std::integral_constant<int, J % NW>{}, kb, [] {});
+                } else {
+                    compute(std::integral_constant<int, J % NX>{}, std::integral_constant<int, J % NW>{}, kb, issue);
+                }
             };
 
-            if constexpr (NW == 3) {
+            if constexpr (NX == 2) {
+                issue_w(std::integral_constant<int, 0>{}, 0);
+                issue_w(std::integral_constant<int, 1>{}, min(1, nkb - 1));
+                issue_x(std::integral_constant<int, 0>{}, 0);
+                issue_w(std::integral_constant<int, 2>{}, min(2, nkb - 1));
+            } else if constexpr (NW == 3) {
                 issue_x(std::integral_constant<int, 0>{}, 0);
                 issue_w(std::integral_constant<int, 0>{}, 0);
                 issue_x(std::integral_constant<int, 1>{}, min(1, nkb - 1));
@@ -296,7 +334,7 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
             // then the remaining steps as nested conditions: the path back to the loop head is
             // always a whole cycle, and a skipped step skips all later ones, so the compiler's
             // count of the loads in flight never merges two different paths before a step.
-            constexpr int U = NW == 3 ? 3 : 12;
+            constexpr int U = NX == 2 ? 4 : NW == 3 ? 3 : 12;  // lcm(NX, NW)
             int kb = 0;
             for (; kb + U <= nkb; kb += U)
                 tg_static_for<0, U>([&](auto Jc) { step(Jc, kb + decltype(Jc)::value); });
@@ -331,6 +369,12 @@ __global__ __launch_bounds__(kTgThreads) void k_grouped_gemm_tiled(GemmArgs g) {
             }
         };
         const int groups = (rows + 63) >> 6;
+        if constexpr (!FP8) {
+            if (groups > 4) {
+                run(std::integral_constant<int, 5>{});
+                continue;
+            }
+        }
         if (groups > 3) run(std::integral_constant<int, 4>{});
         else if (groups > 2) run(std::integral_constant<int, 3>{});
         else if (groups > 1) run(std::integral_constant<int, 2>{});

@@ -19,8 +19,9 @@
 // token count ("vLLM Community Traces H20 MoE Scheduling Inefficiency to Expert-Load Kernel
 // Selection", paragraphs 3-4): an expert with 1..tile_rows rows becomes one tile of the light
 // GEMM kernel, a heavier one (a hot expert of a concentrated routing, or any expert of a large
-// batch) is cut into tiles of at most 256 rows for the heavy kernel, rows spread as evenly as
-// 16-row steps allow.  When the host knows that no expert can exceed light_cap rows (a few
+// batch) is cut into tiles of at most 256 rows for the heavy kernel (bf16 in a launch with many
+// heavy tasks: an expert of 257..320 rows is one tile), rows spread as evenly as 16-row steps
+// allow.  When the host knows that no expert can exceed light_cap rows (a few
 // light tiles), experts above tile_rows are cut into several light tiles instead, and the
 // heavy-tile launches are left out.
 #include "launch.hpp"
@@ -31,8 +32,8 @@ namespace fmoe {
 constexpr int kScanThreads = 1024;
 constexpr int kSmallChunks = 64;  // chunks of the one-workgroup path
 constexpr int kSmallPerWave = kSmallChunks / (kScanThreads / 64);  // chunks per wavefront there
-// LDS ints of scan_and_tile for El local experts: part sums, then three per-expert arrays
-__host__ __device__ constexpr int scan_lds_ints(int El) { return kScanThreads + 3 * El; }
+// LDS ints of scan_and_tile for El local experts: part sums, three per-expert arrays, a flag
+__host__ __device__ constexpr int scan_lds_ints(int El) { return kScanThreads + 3 * El + 1; }
 
 // Phase 1 for one chunk of 64 assignments, by one wavefront.  Writes the chunk's count of
 // every local expert to col[e * col_stride] (zeros included) and returns, for this lane, the
@@ -98,7 +99,7 @@ __device__ __forceinline__ void write_light_split(DevHeader* hdr, int n_light, i
 // and heavy tiles before each expert) is one wavefront's: lane j takes experts j*J .. j*J+J-1
 // (J = ceil(El/64)) in order, then one wavefront scan adds the lanes' sums.  dropped is read by
 // wavefront 0 only.
-__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int light_cap, int heavy_rows,
+__device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int light_cap, int heavy5_min,
                               int rows_estimate, int sparse_rows, long long dropped,
                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                               MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr,
@@ -126,6 +127,7 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
     int* e_rows = sh + kScanThreads;  // [El]: rows of expert e, then its first grouped row
     int* e_light = e_rows + El;       // [El]: its light tiles, then the light tiles before it
     int* e_heavy = e_light + El;      // [El]: its heavy tiles, then the heavy tiles before it
+    int* five = e_heavy + El;         // [1]: experts of 257..320 rows are one tile
     part_sum[threadIdx.x] = s;
     __syncthreads();
     int before = 0, total = 0;  // this part's prefix inside its expert, and the expert total
@@ -135,34 +137,47 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
         total += v;
     }
     // an expert with 1..light_cap rows is cut into light tiles of tile_rows rows (the last one
-    // takes the rest); a heavier one is cut into ceil(total / heavy_rows) tiles of equal size
-    // rounded up to 16 rows (the last one takes the rest), so the tiles of one expert carry
-    // about the same work
+    // takes the rest); a heavier one is cut into ceil(total / 256) tiles of equal size rounded up
+    // to 16 rows (the last one takes the rest), so the tiles of one expert carry about the same
+    // work -- except that an expert of 257..320 rows is one tile of five 64-row groups when
+    // the 256-row tiles of all experts number heavy5_min or more (a launch with several tasks
+    // per compute unit, where one task in place of two saves the second task's weight copies)
     const bool heavy = total > light_cap;
     const int nlight = (total > 0 && !heavy) ? (total + tile_rows - 1) / tile_rows : 0;
-    const int nheavy0 = heavy ? (total + heavy_rows - 1) / heavy_rows : 0;
-    const int hrows = heavy ? min(heavy_rows, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
-    const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0
+    const bool five_able = heavy && total > kHeavyRows && total <= kHeavyRows5;
     if (live && part == 0) {
         e_rows[e] = total;
         e_light[e] = nlight;
-        e_heavy[e] = nheavy;
+        e_heavy[e] = heavy ? (total + kHeavyRows - 1) / kHeavyRows : 0;
     }
     __syncthreads();
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         const int J = (El + 63) >> 6;
         const int ea = min(El, lane * J), eb = min(El, ea + J);
-        int sr = 0, sl = 0, sh_ = 0, lrows = 0, empty = 0, mx = 0;
+        int sr = 0, sl = 0, sh_ = 0, lrows = 0, empty = 0, mx = 0, n5 = 0;
         for (int x = ea; x < eb; x++) {
-            const int r = e_rows[x], l = e_light[x];
+            const int r = e_rows[x], l = e_light[x], h = e_heavy[x];
             sr += r;
             sl += l;
-            sh_ += e_heavy[x];
+            sh_ += h;
+            n5 += h > 0 && r > kHeavyRows && r <= kHeavyRows5;
             lrows += l > 0 ? r : 0;
             empty += r == 0;
             mx = max(mx, r);
         }
+        int all256 = sh_;  // heavy tiles of 256 rows, all experts
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) all256 += __shfl_xor(all256, o, 64);
+        const bool use5 = all256 >= heavy5_min;
+        if (use5 && n5 > 0) {
+            sh_ -= n5;  // two tiles become one
+            for (int x = ea; x < eb; x++) {
+                const int r = e_rows[x];
+                if (e_heavy[x] > 0 && r > kHeavyRows && r <= kHeavyRows5) e_heavy[x] = 1;
+            }
+        }
+        if (lane == 0) *five = use5;
         // inclusive scans of the lanes' sums (rows, light tiles, heavy tiles, light rows, empty experts)
         int ir = sr, il = sl, ih = sh_, ilr = lrows, ie = empty;
 #pragma unroll
@@ -197,12 +212,16 @@ __device__ void scan_and_tile(int* cnt, int nchunk, int El, int tile_rows, int l
             hdr->empty_experts = ie;
             hdr->dropped = dropped;
             hdr->tile_rows = tile_rows;
-            hdr->heavy_rows = heavy_rows;
+            hdr->heavy_rows = use5 ? kHeavyRows5 : kHeavyRows;
             hdr->rows_estimate = rows_estimate;
             write_light_split(hdr, il, ilr, sparse_rows);
         }
     }
     __syncthreads();
+    const int cap = five_able && *five ? kHeavyRows5 : kHeavyRows;
+    const int nheavy0 = heavy ? (total + cap - 1) / cap : 0;
+    const int hrows = heavy ? min(cap, ((total + nheavy0 - 1) / nheavy0 + 15) / 16 * 16) : 1;
+    const int nheavy = heavy ? (total + hrows - 1) / hrows : 0;  // == nheavy0, the count scanned above
     if (live) {
         const int my_first = e_rows[e], my_lfirst = e_light[e], my_hfirst = e_heavy[e];
         int run = my_first + before;
@@ -267,7 +286,7 @@ __device__ __forceinline__ void chunk_scatter(int i, int n, int l, int r, int ba
 // All three phases by one workgroup of kScanThreads.  ids may point to global memory or to
 // LDS (generic addressing); lds holds small_lds_ints(n, El) ints.
 __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, int El, int lo, int tile_rows,
-                                            int light_cap, int heavy_rows, int rows_estimate, int sparse_rows, int32_t* __restrict__ counts,
+                                            int light_cap, int heavy5_min, int rows_estimate, int sparse_rows, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                             int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles,
                                             MTile* __restrict__ mtiles_heavy, DevHeader* __restrict__ hdr, int* lds) {
@@ -307,7 +326,7 @@ __device__ __forceinline__ void group_small(const int32_t* ids, int n, int E, in
         for (int o = 32; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
         dropped = d;
     }
-    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
+    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
                   mtiles_heavy, hdr, sh);
     __syncthreads();
 #pragma unroll
@@ -324,7 +343,7 @@ static size_t small_lds_ints(int n, int El) {
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __restrict__ ids, int n, int E, int El,
-                                                             int lo, int tile_rows, int light_cap, int heavy_rows,
+                                                             int lo, int tile_rows, int light_cap, int heavy5_min,
                                                              int rows_estimate, int sparse_rows,
                                                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm_src,
@@ -332,7 +351,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
                                                              MTile* __restrict__ mtiles_heavy,
                                                              DevHeader* __restrict__ hdr) {
     extern __shared__ int lds[];
-    group_small(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm,
+    group_small(ids, n, E, El, lo, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm,
                 mtiles, mtiles_heavy, hdr, lds);
 }
 
@@ -341,7 +360,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_small(const int32_t* __r
 // those of group_small: the chunk's counts are the expert totals, the exclusive scans over the
 // experts in ascending order give the offsets and the light tile slots, and each assignment
 // goes to its expert's offset plus its rank in the chunk.  cnt: El ints of LDS.
-__device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy_rows,
+__device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int heavy5_min,
                            int rows_estimate, int sparse_rows, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ perm_src, int32_t* __restrict__ inv_perm,
                            MTile* __restrict__ mtiles, DevHeader* __restrict__ hdr, int* cnt) {
@@ -394,7 +413,7 @@ __device__ void group_wave(const int32_t* ids, int n, int E, int El, int lo, int
         hdr->empty_experts = El - run_tiles;
         hdr->dropped = bad;
         hdr->tile_rows = tile_rows;
-        hdr->heavy_rows = heavy_rows;
+        hdr->heavy_rows = kHeavyRows;
         hdr->rows_estimate = rows_estimate;
         write_light_split(hdr, run_tiles, run_rows, sparse_rows);
     }
@@ -413,7 +432,7 @@ constexpr int kWaveGroupTokens = 16;
 template <int SLOTS, bool BF16_IN, bool QX>
 __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
     const void* __restrict__ logits, int T, int E, int k, int scoring, int renorm, int32_t* __restrict__ ids,
-    float* __restrict__ weights, int El, int lo, int tile_rows, int light_cap, int heavy_rows, int rows_estimate, int sparse_rows,
+    float* __restrict__ weights, int El, int lo, int tile_rows, int light_cap, int heavy5_min, int rows_estimate, int sparse_rows,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ inv_perm, MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
     DevHeader* __restrict__ hdr, XQuant xq) {
@@ -430,11 +449,11 @@ __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
     __syncthreads();
     if (n <= 64 && T <= kWaveGroupTokens) {
         if (w == 0)
-            group_wave(ids_lds, n, E, El, lo, tile_rows, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src,
+            group_wave(ids_lds, n, E, El, lo, tile_rows, heavy5_min, rows_estimate, sparse_rows, counts, offsets, perm_src,
                        inv_perm, mtiles, hdr, lds + ((n + 3) & ~3));
         return;
     }
-    group_small(ids_lds, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src,
+    group_small(ids_lds, n, E, El, lo, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, counts, offsets, perm_src,
                 inv_perm, mtiles, mtiles_heavy, hdr, lds + ((n + 3) & ~3));
 }
 
@@ -457,7 +476,7 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int light_cap, int heavy_rows, int rows_estimate, int sparse_rows,
+                                                            int light_cap, int heavy5_min, int rows_estimate, int sparse_rows,
                                                             const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
@@ -472,7 +491,7 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
+    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
                   mtiles_heavy, hdr, sh);
 }
 
@@ -493,13 +512,13 @@ size_t group_scratch_bytes(long long n, int El) {
 }
 
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
-                        int heavy_rows, int rows_estimate, int sparse_rows,
+                        int heavy5_min, int rows_estimate, int sparse_rows,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st) {
     const int nchunk = (n + 63) / 64;
     const size_t lds = small_lds_ints(n, El) * 4;
     if (nchunk <= kSmallChunks && lds <= 65536) {
-        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows,
+        k_group_small<<<1, kScanThreads, lds, st>>>(ids, n, E, El, lo, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows,
                                                     counts,
                                                     offsets,
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
@@ -508,7 +527,7 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
     int* cnt = scratch;                        // [nchunk][El]
     int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
     k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, light_cap, heavy_rows, rows_estimate, sparse_rows, bad,
+    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, bad,
                                              counts,
                                              offsets, mtiles,
                                              mtiles_heavy, hdr);
@@ -531,7 +550,7 @@ bool route_group_fits(int T, int k, int E, int El) {
 template <int SLOTS>
 static void launch_route_group_slots(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                                      int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
-                                     int heavy_rows, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets,
+                                     int heavy5_min, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets,
                                      int32_t* perm_src, int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy,
                                      DevHeader* hdr, hipStream_t st, const XQuant* xq) {
     const size_t lds = route_group_lds_bytes(T, k, El);
@@ -541,13 +560,13 @@ static void launch_route_group_slots(const void* logits, bool bf16, int T, int E
     // workgroup 0 routes and groups; FP8: one more workgroup per 16 groups of x to quantise
     const unsigned blocks = xq ? 1 + (unsigned)((T * (xq->H / 128) + kScanThreads / 64 - 1) / (kScanThreads / 64)) : 1;
     kern<<<blocks, kScanThreads, lds, st>>>(logits, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows,
-                                            light_cap, heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm,
+                                            light_cap, heavy5_min, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm,
                                             mtiles, mtiles_heavy, hdr, xq ? *xq : none);
 }
 
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
-                              int heavy_rows, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int heavy5_min, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                               int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st,
                               const XQuant* xq) {
     if (!route_group_fits(T, k, E, El)) return hipErrorInvalidValue;
@@ -555,7 +574,7 @@ hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k
     const int slots = (E + 63) / 64;
 #define FMOE_RG(S)                                                                                                  \
     launch_route_group_slots<S>(logits, bf16, T, E, k, scoring, renorm, ids, weights, El, lo, tile_rows, light_cap, \
-                                heavy_rows, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy,   \
+                                heavy5_min, rows_estimate, sparse_rows, counts, offsets, perm_src, inv_perm, mtiles, mtiles_heavy,   \
                                 hdr, st, xq)
     if (slots <= 1) FMOE_RG(1);
     else if (slots <= 2) FMOE_RG(2);

@@ -41,7 +41,7 @@ size_t group_scratch_bytes(long long n, int El);
 bool route_group_fits(int T, int k, int E, int El);
 hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k, int scoring, int renorm,
                               int32_t* ids, float* weights, int El, int lo, int tile_rows, int light_cap,
-                              int heavy_rows, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets,
+                              int heavy5_min, int rows_estimate, int sparse_rows, int32_t* counts, int32_t* offsets,
                               int32_t* perm_src, int32_t* inv_perm, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr,
                               hipStream_t st, const XQuant* xq = nullptr);
 // light_cap >= tile_rows: experts with up to light_cap rows are cut into light tiles of tile_rows
@@ -49,7 +49,7 @@ hipError_t launch_route_group(const void* logits, bool bf16, int T, int E, int k
 // gate/up kernel (DevHeader::m_tiles_split) when they hold fewer than sparse_rows rows on
 // average, else to the streaming one (m_tiles_stream); 0: always the streaming one.
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
-                        int heavy_rows, int rows_estimate, int sparse_rows,
+                        int heavy5_min, int rows_estimate, int sparse_rows,
                         int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, int32_t* rank_buf,
                         int* scratch, MTile* mtiles, MTile* mtiles_heavy, DevHeader* hdr, hipStream_t st);
 hipError_t launch_quant_rows(const void* x, bool bf16_in, long long rows, int cols, uint8_t* q, float* s,
@@ -62,7 +62,7 @@ hipError_t launch_grouped_gemm(bool gated, bool fp8, bool out_f32, const GemmArg
 enum StreamOut { kOutBf16 = 0, kOutF32 = 1, kOutE4M3 = 2 };
 hipError_t launch_grouped_gemm_stream(bool gated, bool fp8, int out_mode, const GemmArgs& a, int tile_rows,
                                       int max_tiles, int cus, hipStream_t st);
-// heavy row tiles (up to 256 rows) with both operands tiled through LDS
+// heavy row tiles (up to 320 rows, FP8 256) with both operands tiled through LDS
 hipError_t launch_grouped_gemm_tiled(bool gated, bool fp8, bool out_f32, const GemmArgs& a, int max_tiles, int cus,
                                      hipStream_t st);
 hipError_t launch_combine(const void* Y, const int32_t* inv_perm, const float* w, int T, int k, int H, void* out,

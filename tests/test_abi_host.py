@@ -141,12 +141,14 @@ def test_forward_planned_rejects_bad_plans_before_launching():
                                         ctypes.byref(plan))
     for bad in (fm.fmoe_plan(24, 0, 0), fm.fmoe_plan(0, 3, 0), fm.fmoe_plan(0, 0, 8), fm.fmoe_plan(-16, 1, 1),
                 fm.fmoe_plan(64, 1, 1), fm.fmoe_plan(48, 0, 0), fm.fmoe_plan(0, 0, 0, 2), fm.fmoe_plan(0, 0, 0, -1),
-                fm.fmoe_plan(16, 1, 1, 16)):
+                fm.fmoe_plan(16, 1, 1, 16), fm.fmoe_plan(0, 0, 0, 0, 128), fm.fmoe_plan(0, 0, 0, 0, 512)):
         assert call(s, w, bad) == fm.FMOE_ERR_ARG
     # FP8 with a 65536-deep reduction: 32-row tiles would need 68 KB of activation scales in LDS
     s8 = fm.make_shape(16, 65536, 128, 8, 2, fp8=True)
     w8 = fm.fmoe_weights(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
     assert call(s8, w8, fm.fmoe_plan(32, 0, 0)) == fm.FMOE_ERR_UNSUPPORTED
+    # tiles of five row groups are bf16 only (FP8's activation scales take that LDS)
+    assert call(fm.make_shape(16, 256, 128, 8, 2, fp8=True), w8, fm.fmoe_plan(0, 0, 0, 0, 320)) == fm.FMOE_ERR_UNSUPPORTED
     # a plan with zero tokens is still a no-op
     s0 = fm.make_shape(0, 256, 128, 8, 2)
     assert lib.fmoe_forward_planned(ctypes.byref(s0), None, None, 0, 0, 1, ctypes.byref(w), None, None, None, None, 0,

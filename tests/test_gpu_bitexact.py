@@ -9,7 +9,7 @@
 * Grouped GEMM indexing on integer data (every operand a small integer times a power-of-two
   scale, so every sum is exact in fp32): every kernel -- streaming light tiles, light tiles with
   the reduction split over 2 or 4 wavefronts, several light tiles per expert, heavy tiles of
-  16..256 rows -- gives outputs bit-equal to the oracle's, on every grouped row, with ragged and
+  16..320 rows (320: one tile for an expert of 257..320 rows, bf16) -- gives outputs bit-equal to the oracle's, on every grouped row, with ragged and
   empty experts, repeated and out-of-range ids and an expert-parallel rank.
 """
 import numpy as np
@@ -217,8 +217,9 @@ def test_gate_up_epilogue_codes_match_oracle(T, H, I, E, k, tile):
 # ----------------------------------------------------------------------------- integer-data grouped GEMMs
 
 # rows per local expert: empty, single rows, both sides of every tile size, heavy tiles of
-# 1..4 staged 64-row groups, experts cut into two and three heavy tiles
-COUNTS = [0, 1, 15, 16, 17, 31, 32, 33, 64, 65, 128, 129, 256, 257, 300, 513]
+# 1..4 staged 64-row groups, experts cut into two and three heavy tiles; with one tile for
+# 257..320 rows (bf16 plans with heavy_rows 320) 257 and 320 are tiles of five row groups
+COUNTS = [0, 1, 15, 16, 17, 31, 32, 33, 64, 65, 128, 129, 256, 257, 320, 513]
 
 
 def crafted_ids(counts, T, k, E, seed, lo=0):
@@ -316,10 +317,15 @@ def assert_bits_equal(got: torch.Tensor, ref_f64: np.ndarray, what: str):
                              f"gpu {g[r, c].item()} oracle {ref_f64[r, c]}")
 
 
-PLANS = {  # (tile rows, gate/up split, down split, light tiles per expert)
-    "stream16": (16, 1, 1, 1), "stream32": (32, 1, 1, 1),
-    "split2_16": (16, 2, 2, 1), "split4_32": (32, 4, 4, 1),
+PLANS = {  # (tile rows, gate/up split, down split, light tiles per expert, heavy rows: 320 for bf16)
+    "stream16": (16, 1, 1, 1, 320), "stream32": (32, 1, 1, 1, 256),
+    "split2_16": (16, 2, 2, 1, 256), "split4_32": (32, 4, 4, 1, 320),
 }
+
+
+def plan_for(name: str, fp8: bool):
+    tr, s1, s2, lt, hr = PLANS[name]
+    return fm.fmoe_plan(tr, s1, s2, lt, 0 if fp8 else hr)
 
 
 @pytest.mark.parametrize("H,I", [(256, 384), (640, 256), (1152, 896), (512, 768)])
@@ -328,12 +334,15 @@ PLANS = {  # (tile rows, gate/up split, down split, light tiles per expert)
 def test_integer_grouped_gemm_is_bit_exact(fp8, plan, H, I):
     announce(f"integer grouped GEMM fp8={fp8} plan={plan} H={H} I={I}")
     C = IntCase(T=470, k=4, E=16, H=H, I=I, fp8=fp8, counts=COUNTS, seed=H + I)
-    p = fm.fmoe_plan(*PLANS[plan])
+    p = plan_for(plan, fp8)
     ws = fm.workspace(C.shape)
     out0 = C.gpu_stage(0, p, ws=ws)
     st = fm.fmoe_read_stats(ws)
-    assert st["local_rows"] == C.R == sum(COUNTS) and st["heavy_tiles"] > 0
-    assert st["dropped_ids"] == C.T * C.k - sum(COUNTS)
+    assert st["local_rows"] == C.R == sum(COUNTS) and st["dropped_ids"] == C.T * C.k - sum(COUNTS)
+    five = not fp8 and PLANS[plan][4] == 320
+    heavy = [c for c in COUNTS if c > PLANS[plan][0]]
+    assert st["heavy_rows"] == (320 if five else 256)
+    assert st["heavy_tiles"] == sum(1 if five and 256 < c <= 320 else -(-c // 256) for c in heavy)
     torch.cuda.synchronize()
     ref0 = C.oracle_stage(0)
     assert_bits_equal(out0[:C.R], ref0, "gate/up")
@@ -348,8 +357,8 @@ def test_integer_grouped_gemm_is_bit_exact(fp8, plan, H, I):
 def test_integer_grouped_gemm_expert_parallel_rank(fp8):
     announce(f"integer grouped GEMM, rank 1 of 2, fp8={fp8}")
     C = IntCase(T=470, k=4, E=16, H=384, I=256, fp8=fp8, counts=COUNTS, ep_size=2, ep_rank=1, seed=3)
-    for plan in ("stream32", "split2_16"):
-        p = fm.fmoe_plan(*PLANS[plan])
+    for plan in ("stream16", "split2_16"):
+        p = plan_for(plan, fp8)
         assert C.R == sum(COUNTS[8:])
         assert_bits_equal(C.gpu_stage(0, p)[:C.R], C.oracle_stage(0), f"gate/up {plan}")
         assert_bits_equal(C.gpu_stage(1, p)[:C.R], C.oracle_stage(1), f"down {plan}")

@@ -33,12 +33,19 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128, fp8
     # light tile: 16 rows at one expected row, 32 from two on; from 32 expected rows on, the
     # smallest again (every expert above 16 rows goes to the heavy-tile kernel)
     assert tr == (16 if est == 1 or est >= 32 else 32)
-    hr = st["heavy_rows"]
-    assert hr == 256
     # FP8: caller ids may repeat, so an expert can hold up to T*k rows; when that fits 8 light
     # tiles, every expert is cut into light tiles of tr rows and there are no heavy tiles
     cap = 8 * tr if fp8 and T * k <= 8 * tr else tr
-    heavy = int(sum(-(-c // hr) for c in ref["counts"] if c > cap))  # ceil(c / 256) equal tiles per heavy expert
+    heavy_counts = [int(c) for c in ref["counts"] if c > cap]
+    # heavy experts: ceil(c / 256) tiles of about equal size; bf16 experts of 257..320 rows are
+    # one tile when the 256-row tiles give each compute unit four tasks in the GEMM with the
+    # fewer 128-column blocks
+    n256 = sum(-(-c // 256) for c in heavy_counts)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nb = min(2 * I // 128, H // 128)
+    five = not fp8 and n256 >= -(-4 * cus // nb)
+    assert st["heavy_rows"] == (320 if five else 256)
+    heavy = sum(1 if five and 256 < c <= 320 else -(-c // 256) for c in heavy_counts)
     light = int(sum(-(-c // tr) for c in ref["counts"] if 0 < c <= cap))
     assert st["heavy_tiles"] == heavy
     assert st["m_tiles"] == light + heavy
@@ -59,12 +66,20 @@ def test_group_random_ids_with_duplicates(T, k, E, ep_size, ep_rank, fp8):
 
 
 def test_group_router_ids_full_sizes():
-    for cfg, T, E, k, routing, ep in [(3, 4096, 128, 8, "uniform", 1), (3, 4096, 128, 8, "concentrated", 1),
-                                      (5, 288, 400, 6, "uniform", 8), (5, 288, 400, 6, "concentrated", 8)]:
-        announce(f"group router ids T={T} E={E} k={k} {routing} ep={ep}")
+    # the 128-expert layer (H=2048, I=768) at T=4096: under uniform routing about half the experts
+    # hold 257..320 rows, one tile each
+    for cfg, T, E, k, routing, ep, H, I in [(3, 4096, 128, 8, "uniform", 1, 2048, 768),
+                                            (3, 4096, 128, 8, "concentrated", 1, 2048, 768),
+                                            (3, 4096, 128, 8, "uniform", 1, 256, 128),
+                                            (5, 288, 400, 6, "uniform", 8, 7168, 2048),
+                                            (5, 288, 400, 6, "concentrated", 8, 7168, 2048)]:
+        announce(f"group router ids T={T} E={E} k={k} {routing} ep={ep} H={H} I={I}")
         lg = synth.routed_logits(cfg, T, E, k, routing)
         ids, _ = oracle.router_topk(synth.bf16_bits(lg), k)
-        r, ref = check_group(ids, E, ep, 0)
+        r, ref = check_group(ids, E, ep, 0, H=H, I=I)
+        if (H, routing) == (2048, "uniform"):
+            st = fm.fmoe_read_stats(r["ws"])
+            assert st["heavy_rows"] == 320 and st["heavy_tiles"] < int((ref["counts"] > 256).sum()) + 128
         if routing == "concentrated":
             hot = ref["counts"][:8].sum()
             assert hot >= 0.85 * T * k

@@ -282,17 +282,21 @@ def test_random_small_shapes_match_the_oracle(case):
 
 
 # Heavy row tiles at the shortest reductions and at stage counts that end inside a cycle of the
-# heavy kernel's buffer rings (bf16: 64-deep stages, 12 per cycle; FP8: 128-deep stages, 3 per
-# cycle): K = 128 gives 2 bf16 stages and a single FP8 stage.  About 300 rows per expert, so
-# experts are cut into one or two heavy tiles.
+# heavy kernel's buffer rings (bf16: 64-deep stages, 12 per cycle, 4 for tiles of five 64-row
+# groups; FP8: 128-deep stages, 3 per cycle): K = 128 gives 2 bf16 stages and a single FP8 stage.
+# About 300 rows per expert, so experts are cut into one or two heavy tiles (bf16 with one tile
+# for 257..320 rows forced: tiles of five row groups).
 @pytest.mark.parametrize("H,I", [(128, 128), (128, 384), (640, 256), (1152, 896)])
 @pytest.mark.parametrize("fp8", [False, True])
 def test_heavy_tiles_at_short_and_ragged_reductions(H, I, fp8):
     announce(f"heavy tiles H={H} I={I} fp8={fp8}")
     L = Layer(config=96, T=600, H=H, I=I, E=4, k=2, fp8=fp8)
+    if not fp8:
+        L.plan = fm.fmoe_plan(0, 0, 0, 0, 320)
     ws = fm.workspace(L.shape)
-    fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws)
-    assert fm.fmoe_read_stats(ws)["heavy_tiles"] >= 4
+    L.forward(ws=ws)
+    st = fm.fmoe_read_stats(ws)
+    assert st["heavy_tiles"] >= 4 and st["heavy_rows"] == (256 if fp8 else 320)
     check_layer(L, n_sample=10 ** 6)
 
 
@@ -315,25 +319,34 @@ def test_size_limits_and_large_batches(T, H, I, E, k, fp8, n_sample):
     check_layer(L, n_sample=n_sample)
 
 
-def test_all_assignments_on_one_expert_at_the_assignment_limit():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_all_assignments_on_one_expert_at_the_assignment_limit(fp8):
     # caller ids may repeat: 2^20 tokens x top-8, every id 0, is 2^23 rows (the limit) on one
     # expert, cut into 32768 heavy tiles (the count fills the top 16 bits of the tile field)
     T, H, I, E, k = 1 << 20, 128, 128, 8, 8
-    announce(f"fmoe_experts: {T * k} rows on one expert")
-    L = synth.tiny_layer(4, H, E, I, seed=7)  # weights only
+    announce(f"fmoe_experts: {T * k} rows on one expert, fp8={fp8}")
     x = synth.activations(98, T, H)
     ids = np.zeros((T, k), np.int32)
     wts = np.random.default_rng(3).random((T, k)).astype(np.float32)
-    shape = fm.make_shape(T, H, I, E, k)
+    shape = fm.make_shape(T, H, I, E, k, fp8=fp8)
     ws = fm.workspace(shape)
-    w = fm.ExpertWeights(L["wg"].cuda(), L["wu"].cuda(), L["wd"].cuda())
+    tok = sample_tokens(T, 48)
+    if fp8:
+        q = synth.expert_weights_fp8(4, E, H, I, 0, 7)
+        w = fm.ExpertWeights(*(t.cuda() for t in q))
+        qg, qu, qd, sg, su, sd = (t.numpy() for t in q)
+        ref = oracle.moe_tokens(synth.bf16_bits(x), ids, wts.astype(np.float64), qg, qu, qd, E=E, sg=sg, su=su,
+                                sd=sd, tokens=tok)
+    else:
+        L = synth.tiny_layer(4, H, E, I, seed=7)  # weights only
+        w = fm.ExpertWeights(L["wg"].cuda(), L["wu"].cuda(), L["wd"].cuda())
+        ref = oracle.moe_tokens(synth.bf16_bits(x), ids, wts.astype(np.float64),
+                                *(synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")), E=E, tokens=tok)
     out = fm.fmoe_experts(shape, x.cuda(), torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda(), w, ws=ws)
     st = fm.fmoe_read_stats(ws)
     assert st["local_rows"] == T * k and st["max_rows"] == T * k and st["heavy_tiles"] == T * k // 256
-    tok = sample_tokens(T, 48)
-    ref = oracle.moe_tokens(synth.bf16_bits(x), ids, wts.astype(np.float64),
-                            *(synth.bf16_bits(L[n]) for n in ("wg", "wu", "wd")), E=E, tokens=tok)
-    assert row_rel_err(out.float().cpu().numpy()[tok], ref) <= BF16_TOL
+    assert st["heavy_rows"] == (256 if fp8 else 320)  # bf16: one tile for 257..320 rows (none here)
+    assert row_rel_err(out.float().cpu().numpy()[tok], ref) <= (FP8_TOL if fp8 else BF16_TOL)
     del ws, out
 
 
