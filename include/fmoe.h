@@ -270,9 +270,12 @@ int fmoe_grouped_gemm(const fmoe_shape* shape, const fmoe_plan* plan, int32_t st
 enum {
     FMOE_STAGE_ROUTER = 0, FMOE_STAGE_GROUP = 1, FMOE_STAGE_QUANT_X = 2,
     FMOE_STAGE_GEMM1 = 3,        /* gate/up GEMM of the light row tiles                       */
-    FMOE_STAGE_GEMM1_HEAVY = 4,  /* gate/up GEMM of the heavy row tiles (may find none)       */
-    FMOE_STAGE_QUANT_H = 5, FMOE_STAGE_GEMM2 = 6, FMOE_STAGE_GEMM2_HEAVY = 7, FMOE_STAGE_COMBINE = 8,
-    FMOE_NUM_STAGES = 9
+    FMOE_STAGE_GEMM1_SPLIT = 4,  /* gate/up GEMM of the light row tiles that the grouping gave
+                                    to the split-reduction kernel (few rows per tile on average,
+                                    see fmoe_stats.split_light_tiles; may find none)            */
+    FMOE_STAGE_GEMM1_HEAVY = 5,  /* gate/up GEMM of the heavy row tiles (may find none)       */
+    FMOE_STAGE_QUANT_H = 6, FMOE_STAGE_GEMM2 = 7, FMOE_STAGE_GEMM2_HEAVY = 8, FMOE_STAGE_COMBINE = 9,
+    FMOE_NUM_STAGES = 10
 };
 
 /* fmoe_forward that also records stage_events[i] (hipEvent_t, created by the caller) on the

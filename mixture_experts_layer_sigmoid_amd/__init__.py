@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libfmoe.so")
 FMOE_OK, FMOE_ERR_ARG, FMOE_ERR_UNSUPPORTED, FMOE_ERR_WORKSPACE, FMOE_ERR_HIP = range(5)
 FMOE_BF16, FMOE_FP32, FMOE_FP8_E4M3 = 0, 1, 2
 FMOE_SOFTMAX, FMOE_SIGMOID = 0, 1
-FMOE_NUM_STAGES = 9
-STAGES = ("router", "group", "quant_x", "gemm1", "gemm1_heavy", "quant_h", "gemm2", "gemm2_heavy", "combine")
+FMOE_NUM_STAGES = 10
+STAGES = ("router", "group", "quant_x", "gemm1", "gemm1_split", "gemm1_heavy", "quant_h", "gemm2", "gemm2_heavy",
+          "combine")
 EXPORTED = ("fmoe_abi_version", "fmoe_status_string", "fmoe_workspace_bytes", "fmoe_router_logits",
             "fmoe_router_topk", "fmoe_route_permute", "fmoe_experts", "fmoe_forward", "fmoe_forward_profiled",
             "fmoe_forward_planned", "fmoe_router_topk_grouped", "fmoe_read_stats", "fmoe_act_quant",

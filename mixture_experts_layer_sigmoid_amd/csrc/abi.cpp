@@ -323,9 +323,11 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
         }
         FMOE_TRY(launch_grouped_gemm_stream(true, p.fp8, fused_quant_h ? kOutE4M3 : p.fp8 ? kOutF32 : kOutBf16, g1,
                                             p.tile_rows, p.max_light, cus, st));
+        record(ev, FMOE_STAGE_GEMM1_SPLIT, st);
         if (p.sparse_rows > 0) FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1s, p.tile_rows, 2, p.max_light, cus, st));
     } else {
         FMOE_TRY(launch_grouped_gemm(true, p.fp8, p.fp8, g1, p.tile_rows, p.wk1, p.max_light, cus, st));
+        record(ev, FMOE_STAGE_GEMM1_SPLIT, st);
     }
     record(ev, FMOE_STAGE_GEMM1_HEAVY, st);
     if (heavy_possible) FMOE_TRY(launch_grouped_gemm_tiled(true, p.fp8, p.fp8, g1h, p.max_heavy, cus, st));

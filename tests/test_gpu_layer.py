@@ -374,10 +374,10 @@ def test_profiled_forward_and_hip_graph_replays_match_eager(fp8):
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(fm.FMOE_NUM_STAGES + 1)]
     profiled = fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, stage_events=evs)
     assert torch.equal(profiled, eager)
-    # only the event pair around the light gate/up GEMM (how the benchmark times it)
+    # only the event pair around the streaming gate/up GEMM (how the benchmark times it)
     pair = [None] * (fm.FMOE_NUM_STAGES + 1)
     pair[fm.STAGES.index("gemm1")] = torch.cuda.Event(enable_timing=True)
-    pair[fm.STAGES.index("gemm1_heavy")] = torch.cuda.Event(enable_timing=True)
+    pair[fm.STAGES.index("gemm1_split")] = torch.cuda.Event(enable_timing=True)
     assert torch.equal(fm.fmoe_forward(L.shape, L.x_gpu, L.logits_gpu, L.w, ws=ws, stage_events=pair), eager)
     out = torch.empty_like(eager)
     graph = torch.cuda.CUDAGraph()
