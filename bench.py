@@ -556,8 +556,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-steps", type=int, default=12)
-    ap.add_argument("--roofline-every", type=int, default=4,
-                    help="time the dominant kernel with an event pair on every N-th timed step")
+    ap.add_argument("--roofline-every", type=int, default=3,
+                    help="time the dominant kernel with an event pair on every N-th timed step (3: the "
+                         "sampled steps run through every batch and both weight copies in turn)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --no-sweep --no-cpu --calibrate` into profiles/traffic.json")
@@ -626,6 +627,7 @@ def main():
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                 traffic=traffic_from_profile(head.name, dom), algorithmic_bytes_per_launch=int(alg),
                 avg_launch_us=round(dom_us, 2), timed_launches=len(m["pair_us"]),
+                launch_us=[round(u, 2) for u in m["pair_us"]],
                 stage_breakdown_us={k: round(v, 2) for k, v in m["stage_us"].items()})
 
     sweep = [hs]
