@@ -7,11 +7,12 @@
 // than the average).  With up to 320 rows per tile the work is a dense contraction, so the
 // kernel is built around the matrix cores rather than the weight stream.
 //
-// Shape: one workgroup of 8 wavefronts computes a tile of up to 320 rows (FP8: 256) times 128
-// weight columns (gate/up: 64 features of each matrix, so SiLU-and-mul happens in registers).
-// The tile's rows are staged in NA groups of 64 (NA = 1..5, FP8 1..4); the wavefronts form a 4 x 2 grid, each
-// owning 16*NA rows x 64 columns (4*NA accumulators of 16 x 16), so all 8 wavefronts, and all
-// four SIMDs equally, carry MFMA work whatever the tile's size.
+// Shape: one workgroup of 8 wavefronts computes a tile of up to 256 rows (320 for a bf16 expert
+// of 257..320 rows cut as one tile) times 128 weight columns (gate/up: 64 features of each
+// matrix, so SiLU-and-mul happens in registers).  The tile's rows are staged in NA groups of 64
+// (NA = 1..5, FP8 1..4); the wavefronts form a 4 x 2 grid, each owning 16*NA rows x 64 columns
+// (4*NA accumulators of 16 x 16), so all 8 wavefronts, and all four SIMDs equally, carry MFMA
+// work whatever the tile's size.
 // Every 128-byte slice of the reduction (64 bf16 or 128 e4m3 per row) is one stage: the
 // activation rows (gathered through the row map) and the weight rows are copied straight from
 // global memory into LDS by direct global-to-LDS loads: the activations three stages deep (two
