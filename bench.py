@@ -459,17 +459,20 @@ def router_microbench(samples: int = 24, warmup: int = 5, batch_calls: int = 200
 
 def tile_sweep(workloads, steps: int = 10) -> list:
     """Tile-space sweep: every tile plan the library can run (light tile rows 16/32 x gate/up
-    reduction split 1/2/4 x down split 1/2/4 x light tiles per expert 1/8) against the host
-    heuristic, per workload.  Each
+    reduction split 1/2/4 x down split 1/2/4 x light tiles per expert 1/8, and the heuristic's
+    plan with the heavy-tile cut forced to 256 or 320 rows) against the host heuristic, per
+    workload.  Each
     variant: 2 warmup calls, then `steps` back-to-back calls timed between two events (GPU
     time per call), weights rotating over the workload's copies."""
     import torch
 
     import mixture_experts_layer_sigmoid_amd as fm
 
-    # the heuristic runs first and last (the faster of the two counts), after a warmup of its own
+    # the heuristic runs first and last (the faster of the two counts), after a warmup of its own;
+    # two more plans keep the heuristic's choices but force the heavy-tile cut (256 rows, or one
+    # tile for an expert of 257..320 rows: bf16 only, an FP8 layer rejects it)
     plans = [None] + [(tr, s1, s2, lt) for tr in (16, 32) for s1 in (1, 2, 4) for s2 in (1, 2, 4)
-                      for lt in (1, 8)] + [None]
+                      for lt in (1, 8)] + [(0, 0, 0, 0, 256), (0, 0, 0, 0, 320)] + [None]
     out = []
     for wl in workloads:
         print(f"[bench] tile sweep: {wl.name}", file=sys.stderr, flush=True)
@@ -499,7 +502,12 @@ def tile_sweep(workloads, steps: int = 10) -> list:
                 call(2 + j)
             b.record()
             torch.cuda.synchronize()
-            key = "heuristic" if plan is None else "tile %d, split %d/%d, light tiles %d" % plan
+            if plan is None:
+                key = "heuristic"
+            elif len(plan) == 5:
+                key = "heuristic, heavy tiles of %d rows" % plan[4]
+            else:
+                key = "tile %d, split %d/%d, light tiles %d" % plan
             t = a.elapsed_time(b) * 1e3 / steps
             times[key] = min(t, times.get(key, t))
         best = min((v, k) for k, v in times.items() if k != "heuristic")
