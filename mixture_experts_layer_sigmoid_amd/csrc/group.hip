@@ -458,8 +458,21 @@ __global__ __launch_bounds__(kScanThreads) void k_route_group_small(
 }
 
 // ---------------------------------------------------------------- multi-workgroup path
+//
+// From kBlockPathChunks chunks on, blocks of kBlockChunks chunks, one workgroup each (one
+// wavefront per chunk): the counting launch ranks the block's chunks and sums its counts per
+// expert; the one-workgroup scan runs over those block sums (kBlockChunks times fewer than the chunk counts, which one CU would
+// otherwise read twice and write once: 14 us of the 23 us grouping at 2^15 assignments); the
+// scatter launch turns the block's chunk counts into first grouped rows and places its
+// assignments.
 
-// One wavefront per chunk, 4 per workgroup: counts go to cnt[chunk * El + e], ranks to
+constexpr int kBlockChunks = 8;                  // chunks per block
+constexpr int kBlockThreads = kBlockChunks * 64;  // one wavefront per chunk
+constexpr int kBlockPathChunks = 256;             // from this many chunks on (fewer: the chunk-level
+                                                  // path, whose one-workgroup scan is short there)
+
+// Chunk-level path (fewer than kBlockPathChunks chunks).  Phase 1, one wavefront per chunk,
+// 4 per workgroup: counts go to cnt[chunk * El + e], ranks to
 // rank_buf, the chunk's ids outside [0,E) to bad_buf[chunk].
 __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
                                                      int nchunk, int* __restrict__ cnt, int32_t* __restrict__ rank_buf,
@@ -475,9 +488,42 @@ __global__ __launch_bounds__(256) void k_group_count(const int32_t* __restrict__
     if (lane_id() == 0) bad_buf[chunk] = bad;
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ cnt, int nchunk, int El, int tile_rows,
-                                                            int light_cap, int heavy5_min, int rows_estimate, int sparse_rows,
-                                                            const int* __restrict__ bad_buf,
+// Phase 1 for one block: counts to cnt[chunk * El + e], ranks to rank_buf, the chunk's ids
+// outside [0,E) to bad_buf[chunk], the block's count of each local expert to
+// bsum[block * El + e].
+__global__ __launch_bounds__(kBlockThreads) void k_group_count_blocks(const int32_t* __restrict__ ids, int n, int E, int El,
+                                                                     int lo, int nchunk, int* __restrict__ cnt,
+                                                                     int32_t* __restrict__ rank_buf,
+                                                                     int* __restrict__ bad_buf, int* __restrict__ bsum) {
+    extern __shared__ int lds[];  // [8][El]: one mask per wavefront
+    const int w = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * kBlockChunks, c1 = min(nchunk, c0 + kBlockChunks);
+    if (c0 + w < c1) {
+        const int c = c0 + w;
+        int l, r, bad;
+        chunk_rank(ids, n, E, El, lo, c, cnt + (size_t)c * El, 1, lds + w * El, &l, &r, &bad);
+        const int i = c * 64 + lane_id();
+        if (i < n) rank_buf[i] = r;
+        if (lane_id() == 0) bad_buf[c] = bad;
+    }
+    __syncthreads();  // this workgroup's counts are visible to all its threads
+    for (int e = threadIdx.x; e < El; e += kBlockThreads) {
+        int v[kBlockChunks];
+#pragma unroll
+        for (int j = 0; j < kBlockChunks; j++) v[j] = c0 + j < c1 ? cnt[(size_t)(c0 + j) * El + e] : 0;
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kBlockChunks; j++) sum += v[j];
+        bsum[(size_t)blockIdx.x * El + e] = sum;
+    }
+}
+
+// Phase 2 over a [nblock][El] count matrix (the chunk counts, or the block sums):
+// bsum[block * El + e] becomes the first grouped row of expert e in that chunk or block;
+// counts, offsets, tiles and header as in the one-workgroup path.  bad_buf holds nchunk entries.
+__global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ bsum, int nblock, int nchunk, int El,
+                                                            int tile_rows, int light_cap, int heavy5_min, int rows_estimate,
+                                                            int sparse_rows, const int* __restrict__ bad_buf,
                                                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                             MTile* __restrict__ mtiles, MTile* __restrict__ mtiles_heavy,
                                                             DevHeader* __restrict__ hdr) {
@@ -491,10 +537,41 @@ __global__ __launch_bounds__(kScanThreads) void k_group_scan(int* __restrict__ c
     __syncthreads();
     long long dropped = 0;
     for (int q = 0; q < kScanThreads / 64; q++) dropped += dsum[q];
-    scan_and_tile(cnt, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, dropped, counts, offsets, mtiles,
-                  mtiles_heavy, hdr, sh);
+    scan_and_tile(bsum, nblock, El, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, dropped, counts, offsets,
+                  mtiles, mtiles_heavy, hdr, sh);
 }
 
+// Phase 3 for one block: the first grouped row of each (chunk, expert) is the block's first
+// row of the expert plus the counts of the block's earlier chunks; then every assignment goes
+// to its chunk's row plus its rank.
+__global__ __launch_bounds__(kBlockThreads) void k_group_scatter_blocks(const int32_t* __restrict__ ids, int n, int E, int El,
+                                                                       int lo, int nchunk, int* __restrict__ cnt,
+                                                                       const int* __restrict__ bsum,
+                                                                const int32_t* __restrict__ rank_buf,
+                                                                int32_t* __restrict__ perm_src,
+                                                                int32_t* __restrict__ inv_perm) {
+    const int c0 = blockIdx.x * kBlockChunks, c1 = min(nchunk, c0 + kBlockChunks);
+    for (int e = threadIdx.x; e < El; e += kBlockThreads) {
+        int v[kBlockChunks];  // all loads first, then the stores
+#pragma unroll
+        for (int j = 0; j < kBlockChunks; j++) v[j] = c0 + j < c1 ? cnt[(size_t)(c0 + j) * El + e] : 0;
+        int run = bsum[(size_t)blockIdx.x * El + e];
+#pragma unroll
+        for (int j = 0; j < kBlockChunks; j++) {
+            if (c0 + j < c1) cnt[(size_t)(c0 + j) * El + e] = run;
+            run += v[j];
+        }
+    }
+    __syncthreads();  // this workgroup's first rows are visible to all its threads
+    const int i1 = min(n, c1 * 64);
+    for (int i = c0 * 64 + (int)threadIdx.x; i < i1; i += kBlockThreads) {
+        const int id = ids[i];
+        const int l = (id >= 0 && id < E && id - lo >= 0 && id - lo < El) ? id - lo : -1;
+        chunk_scatter(i, n, l, rank_buf[i], l >= 0 ? cnt[(size_t)(i / 64) * El + l] : 0, perm_src, inv_perm);
+    }
+}
+
+// Chunk-level phase 3: every assignment goes to its chunk's first row of its expert plus its rank.
 __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict__ ids, int n, int E, int El, int lo,
                                                        int nchunk, const int* __restrict__ cnt,
                                                        const int32_t* __restrict__ rank_buf,
@@ -507,8 +584,8 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
 }
 
 size_t group_scratch_bytes(long long n, int El) {
-    const long long nchunk = (n + 63) / 64;
-    return (size_t)(nchunk * El + nchunk) * sizeof(int);
+    const long long nchunk = (n + 63) / 64, nblock = (nchunk + kBlockChunks - 1) / kBlockChunks;
+    return (size_t)(nchunk * El + nchunk + nblock * El) * sizeof(int);
 }
 
 hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int tile_rows, int light_cap,
@@ -524,14 +601,23 @@ hipError_t launch_group(const int32_t* ids, int n, int E, int El, int lo, int ti
                                                     perm_src, inv_perm, mtiles, mtiles_heavy, hdr);
         return hipGetLastError();
     }
-    int* cnt = scratch;                        // [nchunk][El]
-    int* bad = scratch + (size_t)El * nchunk;  // [nchunk]
-    k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
-    k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate, sparse_rows, bad,
-                                             counts,
-                                             offsets, mtiles,
-                                             mtiles_heavy, hdr);
-    k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);
+    int* cnt = scratch;                    // [nchunk][El]
+    int* bad = cnt + (size_t)El * nchunk;  // [nchunk]
+    if (nchunk < kBlockPathChunks) {
+        k_group_count<<<(nchunk + 3) / 4, 256, (size_t)4 * El * 4, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, bad);
+        k_group_scan<<<1, kScanThreads, 0, st>>>(cnt, nchunk, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate,
+                                                 sparse_rows, bad, counts, offsets, mtiles, mtiles_heavy, hdr);
+        k_group_scatter<<<(n + 255) / 256, 256, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, rank_buf, perm_src, inv_perm);
+        return hipGetLastError();
+    }
+    const int nblock = (nchunk + kBlockChunks - 1) / kBlockChunks;
+    int* bsum = bad + nchunk;  // [nblock][El]
+    k_group_count_blocks<<<nblock, kBlockThreads, (size_t)(kBlockThreads / 64) * El * 4, st>>>(ids, n, E, El, lo, nchunk,
+                                                                                                cnt, rank_buf, bad, bsum);
+    k_group_scan<<<1, kScanThreads, 0, st>>>(bsum, nblock, nchunk, El, tile_rows, light_cap, heavy5_min, rows_estimate,
+                                             sparse_rows, bad, counts, offsets, mtiles, mtiles_heavy, hdr);
+    k_group_scatter_blocks<<<nblock, kBlockThreads, 0, st>>>(ids, n, E, El, lo, nchunk, cnt, bsum, rank_buf, perm_src,
+                                                            inv_perm);
     return hipGetLastError();
 }
 

@@ -56,6 +56,9 @@ def check_group(ids: np.ndarray, E: int, ep_size=1, ep_rank=0, H=256, I=128, fp8
     (1, 1, 1, 1, 0), (1, 8, 128, 1, 0), (37, 3, 16, 1, 0), (64, 8, 128, 1, 0), (300, 4, 8, 1, 0),
     (288, 6, 400, 8, 0), (288, 6, 400, 8, 5), (513, 8, 64, 4, 3), (4096, 8, 128, 1, 0), (2000, 2, 1024, 1, 0),
     (512, 8, 128, 1, 0), (1024, 4, 16, 1, 0), (1040, 4, 16, 2, 1),  # 64 chunks (one launch), 65 chunks
+    # from 256 chunks on, blocks of 8 chunks: a ragged last block and chunk, 1024 local experts,
+    # an expert-parallel rank
+    (2083, 8, 128, 1, 0), (4100, 4, 1024, 1, 0), (4133, 7, 400, 8, 5),
 ])
 @pytest.mark.parametrize("fp8", [False, True])  # FP8: several light tiles per expert where they bound it
 def test_group_random_ids_with_duplicates(T, k, E, ep_size, ep_rank, fp8):
