@@ -47,6 +47,7 @@ struct Frag {
     static constexpr int KSTEP = 32;  // reduction depth of one MFMA
     static constexpr int LANE_K = 8;  // consecutive elements per lane
     static constexpr int REGS = 4;
+    static constexpr int EB = 2;  // bytes per element
 };
 template <>
 struct Frag<true> {
@@ -54,6 +55,7 @@ struct Frag<true> {
     static constexpr int KSTEP = 128;
     static constexpr int LANE_K = 32;
     static constexpr int REGS = 8;
+    static constexpr int EB = 1;
 };
 
 template <bool FP8>
@@ -73,7 +75,14 @@ size_t gemm_lds_bytes(bool fp8, int K, int tile_rows) {
 // One row tile: wavefront (wn, wk) computes 16 output features n0..n0+15 over its share of
 // the reduction; NS = active 16-row sub-blocks (compile time, so the reduction loop has no
 // per-step branches).
-template <bool GATED, bool FP8, bool OUT_F32, int NS, int BMS, int WN, int WK>
+//
+// LINE: weights by whole 128-byte lines, as in the streaming kernel (gemm_stream.hip): two
+// non-temporal loads, one of rows 0-7 and one of rows 8-15 of the wavefront's 16, each
+// giving a lower-half lane (r16 < 8) one piece of its own row and an upper-half lane one
+// piece of the row 8 away; a select per dword and a rotation by 8 lanes within each 16-lane
+// row put the MFMA's own pieces back in its lanes.  A line holds two bf16 reduction steps, so
+// a wavefront's share of the reduction must start and end on even steps.
+template <bool GATED, bool FP8, bool OUT_F32, int NS, int BMS, int WN, int WK, bool LINE>
 __device__ __forceinline__ void tile_body(const GemmArgs& g, const MTile& m, int n0, int wn, int wk, float* red,
                                           const float* wsc, const float* asc) {
     using F = Frag<FP8>;
@@ -88,13 +97,46 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const MTile& m, int
     const int s0 = wk * nsteps / WK;
     const int n = (wk + 1) * nsteps / WK - s0;
     const int nkb = g.K >> 7;
-    const size_t wrow = ((size_t)m.expert * g.N + n0 + r16) * g.K + kg * F::LANE_K + (size_t)s0 * F::KSTEP;
+    const bool lower = r16 < 8;
+    // with LINE: the lane's load-A row and piece (an upper-half lane takes the second step's
+    // piece, F::KSTEP elements on), and the distance to its load-B piece, in elements
+    const size_t wrow = LINE ? ((size_t)m.expert * g.N + n0 + (r16 & 7)) * g.K + kg * F::LANE_K +
+                                   (lower ? 0 : F::KSTEP) + (size_t)s0 * F::KSTEP
+                             : ((size_t)m.expert * g.N + n0 + r16) * g.K + kg * F::LANE_K + (size_t)s0 * F::KSTEP;
+    const long long lane_ab = 8 * (long long)g.K + (lower ? F::KSTEP : -F::KSTEP);
 
+    static_assert(!(LINE && FP8), "whole-line loads: bf16 weights");
+    constexpr int PAIR = LINE ? 2 : 1;
+    static_assert(D % PAIR == 0, "the ring holds whole lines");
     FT bw0[D], bw1[D], bx[D][NS];
     float bsa[D][NS], bsw0[D], bsw1[D];
+    // with LINE, slot pairs (s, s+1) load when their second step is issued
     auto issue_w = [&](int slot, int step) {
-        bw0[slot] = load_frag<FP8>(g.W0, wrow + (size_t)step * F::KSTEP);
-        if constexpr (GATED) bw1[slot] = load_frag<FP8>(g.W1, wrow + (size_t)step * F::KSTEP);
+        if constexpr (!LINE) {
+            bw0[slot] = load_frag<FP8>(g.W0, wrow + (size_t)step * F::KSTEP);
+            if constexpr (GATED) bw1[slot] = load_frag<FP8>(g.W1, wrow + (size_t)step * F::KSTEP);
+        } else {
+            if (slot % PAIR != PAIR - 1) return;
+            const size_t e = wrow + (size_t)(step - (PAIR - 1)) * F::KSTEP;
+            auto two = [&](const void* W, FT* bw) {
+                const uint8_t* p = (const uint8_t*)W + e * F::EB;
+                bw[slot - 1] = __builtin_bit_cast(FT, __builtin_nontemporal_load((const i32x4*)p));
+                bw[slot] = __builtin_bit_cast(FT, __builtin_nontemporal_load((const i32x4*)(p + lane_ab * F::EB)));
+            };
+            two(g.W0, bw0);
+            if constexpr (GATED) two(g.W1, bw1);
+        }
+    };
+    // loads A, B of a line into pieces X = lower ? A : B and Y = (lower ? B : A) rotated by 8
+    // lanes within each 16-lane row (row_ror:8)
+    auto regroup = [&](i32x4& a, i32x4& b) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int x = lower ? a[i] : b[i];
+            const int z = lower ? b[i] : a[i];
+            a[i] = x;
+            b[i] = __builtin_amdgcn_update_dpp(0, z, 0x128, 0xf, 0xf, false);
+        }
     };
     size_t xoff[NS];
     auto gather_rows = [&]() {
@@ -122,28 +164,47 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const MTile& m, int
         acc0[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    auto compute = [&](int slot) {
+    // one reduction step on weight fragments w0 (w1) with the slot's activations
+    auto mfma_step = [&](int slot, const FT& w0, const FT& w1) {
 #pragma unroll
         for (int sb = 0; sb < NS; sb++) {
             if constexpr (!FP8) {
-                acc0[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw0[slot], bx[slot][sb], acc0[sb], 0, 0, 0);
+                acc0[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, bx[slot][sb], acc0[sb], 0, 0, 0);
                 if constexpr (GATED)
-                    acc1[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw1[slot], bx[slot][sb], acc1[sb], 0, 0, 0);
+                    acc1[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, bx[slot][sb], acc1[sb], 0, 0, 0);
             } else {
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 p0 =
-                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw0[slot], bx[slot][sb], zero, 0, 0, 0, 0, 0, 0);
+                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w0, bx[slot][sb], zero, 0, 0, 0, 0, 0, 0);
                 const float c0 = bsw0[slot] * bsa[slot][sb];
 #pragma unroll
                 for (int i = 0; i < 4; i++) acc0[sb][i] = __builtin_fmaf(p0[i], c0, acc0[sb][i]);
                 if constexpr (GATED) {
-                    const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bw1[slot], bx[slot][sb], zero,
+                    const f32x4 p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w1, bx[slot][sb], zero,
                                                                                        0, 0, 0, 0, 0, 0);
                     const float c1 = bsw1[slot] * bsa[slot][sb];
 #pragma unroll
                     for (int i = 0; i < 4; i++) acc1[sb][i] = __builtin_fmaf(p1[i], c1, acc1[sb][i]);
                 }
             }
+        }
+    };
+    // step `slot`; with LINE the even slot of a pair runs both of its steps (in order) from
+    // regrouped copies and the odd slot nothing, so no regrouped value has to outlive a branch
+    // of the loop's tail
+    auto compute = [&](int slot) {
+        if constexpr (!LINE) {
+            mfma_step(slot, bw0[slot], bw1[slot]);
+        } else if (slot % 2 == 0) {
+            i32x4 x[2], y[2];
+#pragma unroll
+            for (int h = 0; h < NW; h++) {
+                x[h] = __builtin_bit_cast(i32x4, h ? bw1[slot] : bw0[slot]);
+                y[h] = __builtin_bit_cast(i32x4, h ? bw1[slot + 1] : bw0[slot + 1]);
+                regroup(x[h], y[h]);
+            }
+            mfma_step(slot, __builtin_bit_cast(FT, x[0]), __builtin_bit_cast(FT, x[NW - 1]));
+            mfma_step(slot + 1, __builtin_bit_cast(FT, y[0]), __builtin_bit_cast(FT, y[NW - 1]));
         }
     };
 
@@ -242,7 +303,7 @@ __device__ __forceinline__ void tile_body(const GemmArgs& g, const MTile& m, int
 }
 
 // Persistent workgroups walk the tiles (row tile x 16*WN features) of the device-built list.
-template <bool GATED, bool FP8, bool OUT_F32, int BMS, int WN, int WK>
+template <bool GATED, bool FP8, bool OUT_F32, int BMS, int WN, int WK, bool LINE>
 __global__ __launch_bounds__(256) void k_grouped_gemm(GemmArgs g) {
     static_assert(WN * WK == 4, "four wavefronts per workgroup");
     constexpr int NW = GATED ? 2 : 1;
@@ -279,27 +340,27 @@ __global__ __launch_bounds__(256) void k_grouped_gemm(GemmArgs g) {
         const int n0 = nb * 16 * WN + wn * 16;
         // active sub-blocks rounded up to a power of two (extra columns repeat the last row
         // and are not stored)
-        if (nsub <= 1 || BMS == 1) tile_body<GATED, FP8, OUT_F32, 1, BMS, WN, WK>(g, m, n0, wn, wk, red, wsc, asc);
+        if (nsub <= 1 || BMS == 1) tile_body<GATED, FP8, OUT_F32, 1, BMS, WN, WK, LINE>(g, m, n0, wn, wk, red, wsc, asc);
         else if (nsub <= 2 || BMS == 2)
-            tile_body<GATED, FP8, OUT_F32, (BMS >= 2 ? 2 : 1), BMS, WN, WK>(g, m, n0, wn, wk, red, wsc, asc);
+            tile_body<GATED, FP8, OUT_F32, (BMS >= 2 ? 2 : 1), BMS, WN, WK, LINE>(g, m, n0, wn, wk, red, wsc, asc);
         else if (nsub <= 4 || BMS == 4)
-            tile_body<GATED, FP8, OUT_F32, (BMS >= 4 ? 4 : 1), BMS, WN, WK>(g, m, n0, wn, wk, red, wsc, asc);
-        else tile_body<GATED, FP8, OUT_F32, (BMS >= 8 ? 8 : 1), BMS, WN, WK>(g, m, n0, wn, wk, red, wsc, asc);
+            tile_body<GATED, FP8, OUT_F32, (BMS >= 4 ? 4 : 1), BMS, WN, WK, LINE>(g, m, n0, wn, wk, red, wsc, asc);
+        else tile_body<GATED, FP8, OUT_F32, (BMS >= 8 ? 8 : 1), BMS, WN, WK, LINE>(g, m, n0, wn, wk, red, wsc, asc);
         if (WK > 1 || FP8) __syncthreads();  // LDS is refilled by the next tile
     }
 }
 
 // Persistent grid: the number of workgroups that fit on the GPU at once (occupancy query,
 // cached per instantiation and LDS size), at most the tile bound.
-template <bool GATED, bool FP8, bool OUT_F32, int BMS, int WN, int WK>
-static hipError_t launch_shape(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
+template <bool GATED, bool FP8, bool OUT_F32, int BMS, int WN, int WK, bool LINE>
+static hipError_t launch_grid(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
     const size_t lds = gemm_lds_bytes(FP8, a.K, 16 * BMS);
     static int per_cu = 0;
     static size_t per_cu_lds = 0;
     if (per_cu == 0 || per_cu_lds != lds) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm<GATED, FP8, OUT_F32, BMS, WN, WK>, 256,
-                                                          lds) != hipSuccess || nb < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm<GATED, FP8, OUT_F32, BMS, WN, WK, LINE>,
+                                                          256, lds) != hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
         per_cu_lds = lds;
@@ -308,8 +369,26 @@ static hipError_t launch_shape(const GemmArgs& a, int max_tiles, int cus, hipStr
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    k_grouped_gemm<GATED, FP8, OUT_F32, BMS, WN, WK><<<(unsigned)grid, 256, lds, st>>>(a);
+    k_grouped_gemm<GATED, FP8, OUT_F32, BMS, WN, WK, LINE><<<(unsigned)grid, 256, lds, st>>>(a);
     return hipGetLastError();
+}
+
+// Weight load form: whole lines for bf16 weights, per step for FP8 (there the rearrangement
+// needs more registers than the split kernel's rings leave: the FP8 down GEMM went from 3 to 1
+// wavefronts per SIMD and measured slower), and per step for a bf16 reduction whose four shares
+// would not all start on an even step (K a multiple of 128 but not 256); splits of 1 and 2
+// always do.
+template <bool GATED, bool FP8, bool OUT_F32, int BMS, int WN, int WK>
+static hipError_t launch_shape(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
+    if constexpr (FP8) {
+        return launch_grid<GATED, FP8, OUT_F32, BMS, WN, WK, false>(a, max_tiles, cus, st);
+    } else if constexpr (WK < 4) {
+        return launch_grid<GATED, FP8, OUT_F32, BMS, WN, WK, true>(a, max_tiles, cus, st);
+    } else {
+        if ((a.K / Frag<FP8>::KSTEP) % (2 * WK) == 0)
+            return launch_grid<GATED, FP8, OUT_F32, BMS, WN, WK, true>(a, max_tiles, cus, st);
+        return launch_grid<GATED, FP8, OUT_F32, BMS, WN, WK, false>(a, max_tiles, cus, st);
+    }
 }
 
 template <bool GATED, bool FP8, bool OUT_F32, int BMS>

@@ -51,6 +51,8 @@ struct SCfg {
     static constexpr int LANE_B = 16;  // operand bytes per lane per step
     static constexpr int HALVES = 1;   // 16-byte pieces per lane fragment
     static constexpr int CS = 8;       // steps per staged chunk
+    static constexpr int PAIR = 2;     // steps per 128-byte weight line of a row
+    static constexpr int PART_Y = 64;  // bytes between a lane's two pieces of one line
 };
 template <>
 struct SCfg<true> {
@@ -60,6 +62,8 @@ struct SCfg<true> {
     static constexpr int LANE_B = 32;
     static constexpr int HALVES = 2;
     static constexpr int CS = 4;
+    static constexpr int PAIR = 1;
+    static constexpr int PART_Y = 16;
 };
 
 template <bool FP8, int NS, int CS>
@@ -109,7 +113,7 @@ struct Ctx {
     int soff;              // 0, or the step count for a padding context that re-reads the last step
 };
 
-template <bool GATED, bool FP8, int OUT, int NS, int D, int WV, int CS>
+template <bool GATED, bool FP8, int OUT, int NS, int D, int WV, int CS, bool LINE>
 __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
     using C = SCfg<FP8>;
     using FT = typename C::T;
@@ -172,7 +176,24 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
         }
     };
     const size_t rowbytes = (size_t)K * C::EB;
-    const size_t lane_w = (size_t)r16 * rowbytes + kg * C::LANE_B;
+    // Weight loads by whole lines (LINE): a wavefront's 16 rows x 128 bytes (two bf16 steps,
+    // or one FP8 step) arrive by two non-temporal loads of 8 full 128-byte lines each, load A
+    // rows 0-7 and load B rows 8-15.  The MFMA wants lane (r16, kg) to hold row r16's piece X
+    // (step 2p: bytes 16 kg; FP8: the fragment's low half at 32 kg) and piece Y (step 2p+1:
+    // 64 + 16 kg; FP8: the high half at 32 kg + 16).  In load A a lower-half lane (r16 < 8)
+    // takes piece X of row r16 and an upper-half lane piece Y of row r16 - 8; in load B a
+    // lower-half lane takes piece Y of row r16 + 8 and an upper-half lane piece X of row r16.
+    // So X is A in the lower and B in the upper half lanes, and Y is the other choice seen 8
+    // lanes away (a rotation by 8 within each 16-lane row): the MFMA operands are the bytes a
+    // per-step load gives, in the same lanes.  Non-temporal loads (streamed, not kept in the
+    // caches) raised a plain read of the weights from 5.7-5.8 to 6.6 TB/s, but only with whole
+    // lines per load: with the per-step form (half a line per row and load) the second half
+    // was fetched again, and the down GEMM got slower.  The FP8 gate/up GEMM keeps per-step
+    // loads: its steps are whole lines already, and the rearrangement measured slower there.
+    const bool lower = r16 < 8;
+    const size_t lane_w = LINE ? (size_t)(r16 & 7) * rowbytes + kg * C::LANE_B + (lower ? 0 : C::PART_Y)
+                               : (size_t)r16 * rowbytes + kg * C::LANE_B;
+    const long long lane_ab = 8 * (long long)rowbytes + (lower ? C::PART_Y : -C::PART_Y);
 
     using CT = Ctx<NS, NW>;
     // task i of this workgroup into slot c; past the last task, a padding context that keeps
@@ -216,11 +237,61 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
         c.soff = 0;
     };
 
+    // Ring slot s holds step s's weights.  With LINE, bf16 loads a pair of steps into slots
+    // (s, s+1) (s even) once both are used, FP8 one step (both loads) into its slot; each
+    // arrives as loads A and B and is rearranged into fragments right before its first use.
+    constexpr int PAIR = LINE ? C::PAIR : 1;
+    static_assert(D % PAIR == 0 && CS % PAIR == 0, "ring and chunk hold whole lines");
     FT bw[D][NW];
     auto issue_w = [&](int slot, const CT& c, int step) {
-        const size_t o = (size_t)min(step + c.soff, nsteps - 1) * (C::KSTEP * C::EB);
+        if constexpr (!LINE) {
+            const size_t o = (size_t)min(step + c.soff, nsteps - 1) * (C::KSTEP * C::EB);
 #pragma unroll
-        for (int h = 0; h < NW; h++) bw[slot][h] = *(const FT*)(c.w[h] + o);
+            for (int h = 0; h < NW; h++) bw[slot][h] = *(const FT*)(c.w[h] + o);
+        } else {
+            if (slot % PAIR != PAIR - 1) return;
+            const int s0 = step - (PAIR - 1);  // first step of the line; bf16 step counts are even
+            const size_t o = (size_t)min(s0 + c.soff, nsteps - PAIR) * (C::KSTEP * C::EB);
+#pragma unroll
+            for (int h = 0; h < NW; h++) {
+                const i32x4 a = __builtin_nontemporal_load((const i32x4*)(c.w[h] + o));
+                const i32x4 b = __builtin_nontemporal_load((const i32x4*)(c.w[h] + lane_ab + o));
+                if constexpr (FP8) {
+                    bw[slot][h] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+                } else {
+                    bw[slot - 1][h] = __builtin_bit_cast(bf16x8, a);
+                    bw[slot][h] = __builtin_bit_cast(bf16x8, b);
+                }
+            }
+        }
+    };
+    // loads A, B of a line into pieces X, Y: X = lower ? A : B; Y = (lower ? B : A) rotated by 8
+    // lanes within each 16-lane row (a row_ror:8 move)
+    auto regroup = [&](i32x4& a, i32x4& b) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int x = lower ? a[i] : b[i];
+            const int z = lower ? b[i] : a[i];
+            a[i] = x;
+            b[i] = __builtin_amdgcn_update_dpp(0, z, 0x128, 0xf, 0xf, false);
+        }
+    };
+    auto prepare = [&](int slot) {
+#pragma unroll
+        for (int h = 0; h < NW && LINE; h++) {
+            if constexpr (FP8) {
+                i32x4 a = {bw[slot][h][0], bw[slot][h][1], bw[slot][h][2], bw[slot][h][3]};
+                i32x4 b = {bw[slot][h][4], bw[slot][h][5], bw[slot][h][6], bw[slot][h][7]};
+                regroup(a, b);
+                bw[slot][h] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            } else if (slot % 2 == 0) {
+                i32x4 a = __builtin_bit_cast(i32x4, bw[slot][h]);
+                i32x4 b = __builtin_bit_cast(i32x4, bw[slot + 1][h]);
+                regroup(a, b);
+                bw[slot][h] = __builtin_bit_cast(bf16x8, a);
+                bw[slot + 1][h] = __builtin_bit_cast(bf16x8, b);
+            }
+        }
     };
 
     // staging of one chunk: wavefront w loads pieces w*FPW .. w*FPW+FPW-1; piece f is step
@@ -272,6 +343,7 @@ __global__ __launch_bounds__(64 * WV) void k_grouped_gemm_stream(GemmArgs g) {
             for (int h = 0; h < NW; h++) acc[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
     auto compute = [&](int slot, int buf, int s) {
+        prepare(slot);
 #pragma unroll
         for (int sb = 0; sb < NS; sb++) {
             FT xb;
@@ -442,10 +514,11 @@ constexpr int stream_waves() { return GATED && OUT != kOutE4M3 ? 4 : 8; }
 template <bool GATED, bool FP8, int OUT, int NS, int CS, int D>
 hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t st) {
     constexpr int WV = stream_waves<GATED, OUT>();
+    constexpr bool LINE = !(GATED && FP8);
     static int per_cu = 0;
     if (per_cu == 0) {
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT, NS, D, WV, CS>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_grouped_gemm_stream<GATED, FP8, OUT, NS, D, WV, CS, LINE>,
                                                           64 * WV, 0) != hipSuccess || nb < 1)
             nb = 1;
         per_cu = nb;
@@ -454,7 +527,7 @@ hipError_t launch_stream(const GemmArgs& a, int max_tiles, int cus, hipStream_t 
     const long long cap = (long long)cus * per_cu;
     if (grid > cap) grid = cap;
     grid = (grid + 7) / 8 * 8;  // a multiple of 8 for the per-XCD task order (extra workgroups exit)
-    k_grouped_gemm_stream<GATED, FP8, OUT, NS, D, WV, CS><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
+    k_grouped_gemm_stream<GATED, FP8, OUT, NS, D, WV, CS, LINE><<<(unsigned)grid, 64 * WV, 0, st>>>(a);
     return hipGetLastError();
 }
 
