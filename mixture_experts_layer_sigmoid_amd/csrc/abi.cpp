@@ -113,16 +113,15 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr, long long max
     // expected row (T=8: 118 -> 111 us).  FP8 tiles stream best unsplit at a 2048-deep
     // reduction (T=128: 141 against 150 us split), but a gate/up reduction of 4096 or more
     // splits better in two (the 7168-wide expert shard at T=288: 433 against 440 us uniform,
-    // 325 against 331 us concentrated).
+    // 325 against 331 us concentrated).  At one expected row per expert (T=8) the bf16 gate/up
+    // GEMM splits in two as well: 95.2 against 100.5 us with a split of 4 under uniform
+    // routing, 45.4 against 43.2 us under concentrated routing (whole-line weight loads; with
+    // per-step loads four had been as fast under uniform routing and faster when concentrated).
     const long long local_rows = (p.n * p.El + p.E - 1) / p.E;
     const long long active = local_rows < p.El ? local_rows : p.El;
     auto pick_wk = [&](int N, bool gate_up) {
         const long long tasks = active * (N / 16);
         if (tasks < 1024) return 4;
-        // one expected row per expert: each expert's gate/up weights serve a single row, and
-        // four wavefronts per stream were as fast under uniform routing and faster under
-        // concentrated routing (T=8: 107.6 / 47.9 us against 107.0 / 50.7 us split in two)
-        if (!p.fp8 && gate_up && p.rows_estimate <= 1) return 4;
         // from 128 expected rows on the light tiles are the few experts left below 17 rows, each
         // a short stream: splits of 4 (gate/up) and 2 (down) measured best under uniform and
         // concentrated routing (T=4096: 537 / 603 us against 540 / 620 us with 2 and 1)
