@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfmoe.so")
-SOURCES = ["router.hip", "group.hip", "quant.hip", "gemm.hip", "gemm_stream.hip", "gemm_tiled.hip", "combine.hip", "abi.cpp"]
+SOURCES = ["router.hip", "group.hip", "quant.hip", "gemm.hip", "gemm_stream.hip", "gemm_tiled.hip", "combine.hip", "down_combine.hip",
+           "abi.cpp"]
 ARCH = "gfx950"
 
 

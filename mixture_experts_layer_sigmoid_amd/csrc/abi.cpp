@@ -53,6 +53,7 @@ struct Plan {
     int wk1, wk2;        // wavefronts splitting the reduction of the gate/up and down GEMMs
     int sparse_rows;     // > 0: the forward also launches the split gate/up kernel (split 2) for
                          // light tiles of fewer rows than this on average (decided on the device)
+    bool down_combine;   // the down GEMM and the combine in one launch (small bf16 batches)
     Layout L;
 };
 
@@ -165,6 +166,9 @@ Plan make_plan(const fmoe_shape* s, const fmoe_plan* ov = nullptr, long long max
     if (nh > p.n) nh = p.n;
     p.max_light = (int)(nl < 1 ? 1 : nl);
     p.max_heavy = (int)(nh < 1 ? 1 : nh);
+    // A few assignments (bf16): the down GEMM is a matrix-vector stream, and the combine joins
+    // it in the same launch (down_combine.hip), unless a plan asks for a down split.
+    p.down_combine = down_combine_fits(p.fp8, p.n, p.I) && !(ov && ov->split_down);
 
     Layout& L = p.L;
     size_t o = 0;
@@ -240,9 +244,10 @@ void log_plan(const char* who, const Plan& p) {
     std::fprintf(stderr,
                  "[fmoe] %s: T=%d H=%d I=%d E=%d k=%d E_loc=%d first_expert=%d %s | rows_estimate=%d "
                  "tile_rows=%d light_cap=%d heavy_launch=%d heavy5=%d split_gate_up=%d split_down=%d "
-                 "sparse_rows=%d max_light_tiles=%d max_heavy_tiles=%d workspace=%zu B\n",
+                 "sparse_rows=%d down_combine=%d max_light_tiles=%d max_heavy_tiles=%d workspace=%zu B\n",
                  who, p.T, p.H, p.I, p.E, p.k, p.El, p.lo, p.fp8 ? "fp8" : "bf16", p.rows_estimate, p.tile_rows,
-                 p.light_cap, (int)p.heavy_launch, p.heavy5, p.wk1, p.wk2, p.sparse_rows, p.max_light, p.max_heavy,
+                 p.light_cap, (int)p.heavy_launch, p.heavy5, p.wk1, p.wk2, p.sparse_rows, (int)p.down_combine, p.max_light,
+                 p.max_heavy,
                  p.L.total);
 }
 
@@ -336,6 +341,14 @@ int run_experts(const Plan& p, const void* x, const int32_t* ids, const float* w
         FMOE_TRY(launch_quant_rows(ws + L.h, false, p.n, p.I, (uint8_t*)(ws + L.hq), (float*)(ws + L.hs), hdr, st));
 
     record(ev, FMOE_STAGE_GEMM2, st);
+    if (p.down_combine) {
+        FMOE_TRY(launch_down_combine(ws + L.h, w->down, p.H, p.I, mtiles, mtiles_heavy, hdr, inv, wts, p.T, p.k, out,
+                                     st));
+        record(ev, FMOE_STAGE_GEMM2_HEAVY, st);
+        record(ev, FMOE_STAGE_COMBINE, st);
+        record(ev, FMOE_NUM_STAGES, st);
+        return FMOE_OK;
+    }
     GemmArgs g2;
     g2.A = p.fp8 ? (const void*)(ws + L.hq) : (const void*)(ws + L.h);
     g2.A_scale = p.fp8 ? (const float*)(ws + L.hs) : nullptr;

@@ -67,5 +67,14 @@ hipError_t launch_grouped_gemm_tiled(bool gated, bool fp8, bool out_f32, const G
                                      hipStream_t st);
 hipError_t launch_combine(const void* Y, const int32_t* inv_perm, const float* w, int T, int k, int H, void* out,
                           hipStream_t st);
+// Down GEMM and combine in one launch for small batches (bf16 weights, at most
+// kDownCombineMaxRows assignments, I at most kDownCombineMaxInter): h [R, I] grouped bf16 rows,
+// the light and heavy tile lists with their counts in hdr, out [T, H] bf16.
+constexpr int kDownCombineMaxRows = 64;
+constexpr int kDownCombineMaxInter = 1024;
+bool down_combine_fits(bool fp8, long long n, int I);
+hipError_t launch_down_combine(const void* h, const void* Wd, int H, int I, const MTile* tiles,
+                               const MTile* tiles_heavy, const DevHeader* hdr, const int32_t* inv_perm,
+                               const float* wts, int T, int k, void* out, hipStream_t st);
 
 }  // namespace fmoe
