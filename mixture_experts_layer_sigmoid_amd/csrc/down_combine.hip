@@ -52,6 +52,8 @@ __global__ __launch_bounds__(kDcThreads) void k_down_combine(const uint16_t* __r
     // h rows (16-byte pieces, I/8 per row); partial sums [wavefront][row][feature]
     __shared__ i32x4 Hs[kDownCombineMaxRows * 32 * PP];
     __shared__ float Yp[4 * kDownCombineMaxRows * kDcFeat];
+    __shared__ int32_t Pl[kDownCombineMaxRows];  // inv_perm and routing weights of the T*k <= 64
+    __shared__ float Wl[kDownCombineMaxRows];    // assignments, for the combine
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -132,6 +134,16 @@ __global__ __launch_bounds__(kDcThreads) void k_down_combine(const uint16_t* __r
         }
     };
 
+    // the combine's inputs, loaded first (the oldest loads: they have landed before any wait
+    // below is satisfied) and put in LDS at the end
+    const int n = T * k;
+    int32_t my_p = -1;
+    float my_w = 0.0f;
+    if (tid < n) {
+        my_p = inv_perm[tid];
+        my_w = wts[tid];
+    }
+
     if (nt > 0) {
         i32x4 wa[kDcP][PP], wb[kDcP][PP];
         // the grouped activation rows, straight into LDS: wavefront w copies pieces q0 + lane of
@@ -169,6 +181,10 @@ __global__ __launch_bounds__(kDcThreads) void k_down_combine(const uint16_t* __r
             compute_step(wa, i0 + kDcP);
         }
     }
+    if (tid < n) {
+        Pl[tid] = my_p;
+        Wl[tid] = my_w;
+    }
     __syncthreads();
 
     // combine: thread (token t, feature g) over the token's k assignments in ascending j; y of
@@ -177,12 +193,12 @@ __global__ __launch_bounds__(kDcThreads) void k_down_combine(const uint16_t* __r
         const int t = idx >> 3, g = idx & 7;
         float acc = 0.0f;
         for (int jj = 0; jj < k; jj++) {
-            const int p = inv_perm[(size_t)t * k + jj];
+            const int p = Pl[t * k + jj];
             if (p < 0) continue;
             float y = Yp[(size_t)p * kDcFeat + g];
 #pragma unroll
             for (int ww = 1; ww < 4; ww++) y += Yp[((size_t)ww * kDownCombineMaxRows + p) * kDcFeat + g];
-            acc = __builtin_fmaf(wts[(size_t)t * k + jj], y, acc);
+            acc = __builtin_fmaf(Wl[t * k + jj], y, acc);
         }
         out[(size_t)t * H + f0 + g] = f32_to_bf16(acc);
     }

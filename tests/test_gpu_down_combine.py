@@ -1,6 +1,6 @@
 """The down GEMM and the combine in one launch (bf16, at most 64 assignments): every token of
-every case against the oracle, against the two-launch path (the same call with the down split
-set by a plan), and bit for bit against itself on repeated calls.
+every case against the oracle, against the two-launch path (the same call with the reduction
+splits set by a plan), and bit for bit against itself on repeated calls.
 
 Cases: the 2048 x 768, 128-expert top-8 layer at 1..8 tokens (uniform and concentrated), every
 count of 16-byte pieces per lane (I = 128 .. 1024, ragged ones included: I = 384 leaves half of
@@ -20,15 +20,16 @@ from gpu_common import BF16_TOL, Layer, announce, check_layer, row_rel_err
 pytestmark = pytest.mark.gpu
 
 
-def split_down_plan():
+def split_plan():
     p = fm.fmoe_plan()
-    p.split_down = 2  # a down split in the plan keeps the two-launch path
+    p.split_gate_up = 2  # a down split in the plan keeps the down GEMM and the combine apart
+    p.split_down = 2
     return p
 
 
 def two_paths(L: Layer):
     fused, ids, _ = L.forward()
-    L.plan = split_down_plan()
+    L.plan = split_plan()
     plain, ids2, _ = L.forward()
     L.plan = None
     torch.cuda.synchronize()
@@ -51,6 +52,15 @@ def test_fused_down_combine_every_piece_count(I):
     announce(f"down+combine: I={I}")
     L = Layer(config=96, T=7, H=384, I=I, E=16, k=4, seed=I)
     check_layer(L, n_sample=7)
+
+
+@pytest.mark.parametrize("H", [128, 256, 640, 1280, 1664, 2048, 2560])
+def test_fused_down_combine_every_hidden_size(H):
+    announce(f"down+combine: H={H} (H/8 workgroups)")
+    L = Layer(config=94, T=5, H=H, I=256, E=16, k=4, seed=H)
+    check_layer(L, n_sample=5)
+    fused, plain = two_paths(L)
+    assert row_rel_err(fused, plain) <= BF16_TOL
 
 
 @pytest.mark.parametrize("ep_rank", [0, 3, 7])
@@ -113,3 +123,10 @@ def test_fused_down_combine_is_deterministic():
     for _ in range(20):
         again, _, _ = L.forward()
         assert torch.equal(first, again)
+
+
+def test_fused_down_combine_top2_of_32_tokens():
+    # 32 tokens of top-2: 64 assignments, one or two rows for most experts
+    announce("down+combine: T=32 H=1280 k=2")
+    L = Layer(config=93, T=32, H=1280, I=256, E=16, k=2, seed=32)
+    check_layer(L, n_sample=32)
