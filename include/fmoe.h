@@ -166,7 +166,10 @@ int fmoe_route_permute(const fmoe_shape* shape, const int32_t* topk_ids, int32_t
  *   topk_weights[t,j] * W_down[l] (silu(W_gate[l] x[t]) * (W_up[l] x[t])),  l = id - ep_rank*E_loc,
  * computed as grouping -> (FP8: per-token per-128 e4m3 quantisation of x) -> grouped gate/up
  * GEMM with fused SiLU-and-mul -> (FP8: quantisation of the activation) -> grouped down GEMM ->
- * weighted combine in fp32, rounded once to bf16.  Tokens with no local id get zeros.
+ * weighted combine in fp32, rounded once to bf16.  Tokens with no local id get zeros.  With bf16
+ * weights and at most 64 assignments (T*k <= 64, I <= 1024) the down GEMM and the combine are one
+ * launch that keeps each row's down projection in fp32 (no bf16 rounding before the weighted
+ * sum); results equal the two-launch path's within the layer's rounding.
  *   x [T,H] bf16 (16-byte aligned); topk_ids [T,k] int32; topk_weights [T,k] fp32;
  *   out [T,H] bf16 (16-byte aligned); ws of at least fmoe_workspace_bytes(shape). */
 int fmoe_experts(const fmoe_shape* shape, const void* x, const int32_t* topk_ids,
@@ -239,7 +242,8 @@ int fmoe_act_quant(const void* x, int32_t x_dtype, int64_t rows, int32_t cols, u
  *       quantised it in a separate pass (some expert could take a heavy row tile);
  *   h_codes [T*k,I] e4m3, h_scales [T*k,I/128] fp32 (FP8): the quantised activation;
  *   h_bf16 [T*k,I] bf16 (bf16 weights): the activation;
- *   y [T*k,H] bf16: the down projection of grouped row p (before the routing weight);
+ *   y [T*k,H] bf16: the down projection of grouped row p (before the routing weight); not
+ *       written when the down GEMM and the combine ran as one launch (bf16, T*k <= 64);
  *   perm_src, inv_perm [T*k] int32: the grouping (as fmoe_route_permute).
  * Only the first R grouped rows (fmoe_read_stats local_rows) hold data. */
 typedef struct {
